@@ -1,0 +1,211 @@
+"""Python binding of the fp8blk C ABI (include/fp8blk.h).
+
+Argument marshalling only: every function here forwards torch tensors'
+device pointers, sizes and the current HIP stream to the native entry point
+of the same name in ``libfp8blk.so``; all arithmetic runs in the library's
+HIP kernels.  PyTorch supplies device memory and streams.  There is no CPU
+fallback: if the library is missing, every call raises.
+
+Block kinds, E8M0 rules and output types mirror the C enums.
+"""
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "FP8_BLOCK_1x32_E8M0", "FP8_BLOCK_1x128_F32", "FP8_BLOCK_128x128_F32",
+    "FP8_E8M0_CEIL", "FP8_E8M0_FLOOR", "FP8_OUT_BF16", "FP8_OUT_F32",
+    "Fp8Error", "library", "library_path",
+    "fp8_block_quantize", "fp8_fake_quant_merge", "fp8_block_scaled_gemm", "fp8_grouped_gemm",
+    "fp8_status_string", "fp8_abi_version",
+    "quantize", "fake_quant_merge", "block_scaled_gemm", "grouped_gemm", "scale_shape",
+]
+
+FP8_OK = 0
+FP8_BLOCK_1x32_E8M0, FP8_BLOCK_1x128_F32, FP8_BLOCK_128x128_F32 = 0, 1, 2
+FP8_E8M0_CEIL, FP8_E8M0_FLOOR = 0, 1
+FP8_OUT_BF16, FP8_OUT_F32 = 0, 1
+ABI_VERSION = 1
+
+_KIND_NAMES = {"1x32": FP8_BLOCK_1x32_E8M0, "1x128": FP8_BLOCK_1x128_F32, "128x128": FP8_BLOCK_128x128_F32}
+_RULE_NAMES = {"ceil": FP8_E8M0_CEIL, "floor": FP8_E8M0_FLOOR}
+
+library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfp8blk.so")
+
+_lib = None
+
+
+class Fp8Error(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: fp8blk status {status} ({_status_text(status)})")
+
+
+def library():
+    """The loaded ctypes library (loads it on first use; raises if absent)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(library_path):
+            raise ImportError(f"{library_path} is not built; run `python -m block_scaled_fp8_amax_amd._build`")
+        lib = ctypes.CDLL(library_path)
+        i64, vp, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+        lib.fp8_block_quantize.argtypes = [vp, i64, i64, ci, ci, vp, vp, vp, vp]
+        lib.fp8_block_quantize.restype = ci
+        lib.fp8_fake_quant_merge.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, vp, vp]
+        lib.fp8_fake_quant_merge.restype = ci
+        lib.fp8_block_scaled_gemm.argtypes = [vp, vp, ci, vp, vp, ci, i64, i64, i64, vp, ci, vp]
+        lib.fp8_block_scaled_gemm.restype = ci
+        lib.fp8_grouped_gemm.argtypes = [vp, vp, ci, vp, vp, ci, vp, i64, i64, i64, i64, vp, ci, vp]
+        lib.fp8_grouped_gemm.restype = ci
+        lib.fp8_status_string.argtypes = [ci]
+        lib.fp8_status_string.restype = ctypes.c_char_p
+        lib.fp8_abi_version.argtypes = []
+        lib.fp8_abi_version.restype = ci
+        if lib.fp8_abi_version() != ABI_VERSION:
+            raise ImportError("libfp8blk.so ABI version mismatch")
+        _lib = lib
+    return _lib
+
+
+def _status_text(status):
+    try:
+        return library().fp8_status_string(int(status)).decode()
+    except Exception:  # noqa: BLE001 - only used for error text
+        return "?"
+
+
+def fp8_status_string(status):
+    return library().fp8_status_string(int(status)).decode()
+
+
+def fp8_abi_version():
+    return library().fp8_abi_version()
+
+
+def _kind(k):
+    return _KIND_NAMES[k] if isinstance(k, str) else int(k)
+
+
+def _rule(r):
+    return _RULE_NAMES[r] if isinstance(r, str) else int(r)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream, *tensors):
+    if stream is not None:
+        return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    for t in tensors:
+        if t is not None and t.is_cuda:
+            return torch.cuda.current_stream(t.device).cuda_stream
+    return None
+
+
+def _check(status, where):
+    if status != FP8_OK:
+        raise Fp8Error(status, where)
+
+
+def _contig(*ts):
+    for t in ts:
+        if t is not None and not t.is_contiguous():
+            raise ValueError("fp8blk expects contiguous tensors")
+
+
+# ------------------------------------------------------------ the four calls
+
+def fp8_block_quantize(x, kind, rule, q, scale, xdq=None, stream=None):
+    """x: bf16 [rows, cols]; q: uint8/float8_e4m3fn [rows, cols]; scale: uint8
+    (1x32) or float32 of the kind's shape; xdq: optional bf16 [rows, cols]."""
+    _contig(x, q, scale, xdq)
+    rows, cols = x.shape
+    st = library().fp8_block_quantize(_ptr(x), rows, cols, _kind(kind), _rule(rule), _ptr(q), _ptr(scale),
+                                      _ptr(xdq), _stream(stream, x))
+    _check(st, "fp8_block_quantize")
+
+
+def fp8_fake_quant_merge(w, lora_b, lora_a, q, scale, wdq=None, stream=None):
+    """w: bf16 [n, k]; lora_b bf16 [n, r]; lora_a bf16 [r, k]; q [n, k];
+    scale float32 [n/128, k/128]; wdq optional bf16 [n, k]."""
+    _contig(w, lora_b, lora_a, q, scale, wdq)
+    n, k = w.shape
+    r = lora_a.shape[0]
+    st = library().fp8_fake_quant_merge(_ptr(w), _ptr(lora_b), _ptr(lora_a), n, k, r, _ptr(q), _ptr(scale),
+                                        _ptr(wdq), _stream(stream, w))
+    _check(st, "fp8_fake_quant_merge")
+
+
+def fp8_block_scaled_gemm(a_q, a_scale, a_kind, b_q, b_scale, b_kind, y, stream=None):
+    """Y[m, n] = deq(A) . deq(B)^T; y is bf16 or float32 [m, n]."""
+    _contig(a_q, a_scale, b_q, b_scale, y)
+    m, k = a_q.shape
+    n = b_q.shape[0]
+    y_type = FP8_OUT_F32 if y.dtype == torch.float32 else FP8_OUT_BF16
+    st = library().fp8_block_scaled_gemm(_ptr(a_q), _ptr(a_scale), _kind(a_kind), _ptr(b_q), _ptr(b_scale),
+                                         _kind(b_kind), m, n, k, _ptr(y), y_type, _stream(stream, a_q))
+    _check(st, "fp8_block_scaled_gemm")
+
+
+def fp8_grouped_gemm(a_q, a_scale, a_kind, b_q, b_scale, b_kind, group_offsets, y, stream=None):
+    """a_q [total_m, k]; b_q [groups, n, k]; group_offsets int32 [groups+1]
+    on the device; y bf16/float32 [total_m, n]."""
+    _contig(a_q, a_scale, b_q, b_scale, group_offsets, y)
+    total_m, k = a_q.shape
+    groups, n = b_q.shape[0], b_q.shape[1]
+    if group_offsets.dtype != torch.int32:
+        raise ValueError("group_offsets must be int32")
+    y_type = FP8_OUT_F32 if y.dtype == torch.float32 else FP8_OUT_BF16
+    st = library().fp8_grouped_gemm(_ptr(a_q), _ptr(a_scale), _kind(a_kind), _ptr(b_q), _ptr(b_scale),
+                                    _kind(b_kind), _ptr(group_offsets), groups, total_m, n, k, _ptr(y), y_type,
+                                    _stream(stream, a_q))
+    _check(st, "fp8_grouped_gemm")
+
+
+# --------------------------------------------- allocating conveniences (torch)
+
+def scale_shape(rows, cols, kind):
+    kind = _kind(kind)
+    if kind == FP8_BLOCK_1x32_E8M0:
+        return (rows, cols // 32), torch.uint8
+    if kind == FP8_BLOCK_1x128_F32:
+        return (rows, cols // 128), torch.float32
+    return (rows // 128, cols // 128), torch.float32
+
+
+def quantize(x, block="1x128", rule="ceil", dequant=False, stream=None):
+    """Allocate outputs and run fp8_block_quantize: returns (q, scale[, xdq])
+    with q viewed as torch.float8_e4m3fn."""
+    rows, cols = x.shape
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    shp, dt = scale_shape(rows, cols, block)
+    scale = torch.empty(shp, dtype=dt, device=x.device)
+    xdq = torch.empty_like(x) if dequant else None
+    fp8_block_quantize(x, block, rule, q, scale, xdq, stream)
+    q = q.view(torch.float8_e4m3fn)
+    return (q, scale, xdq) if dequant else (q, scale)
+
+
+def fake_quant_merge(w, lora_b, lora_a, dequant=False, stream=None):
+    n, k = w.shape
+    q = torch.empty((n, k), dtype=torch.uint8, device=w.device)
+    scale = torch.empty((n // 128, k // 128), dtype=torch.float32, device=w.device)
+    wdq = torch.empty_like(w) if dequant else None
+    fp8_fake_quant_merge(w, lora_b, lora_a, q, scale, wdq, stream)
+    q = q.view(torch.float8_e4m3fn)
+    return (q, scale, wdq) if dequant else (q, scale)
+
+
+def block_scaled_gemm(a_q, a_scale, a_kind, b_q, b_scale, b_kind, out_dtype=torch.bfloat16, stream=None):
+    y = torch.empty((a_q.shape[0], b_q.shape[0]), dtype=out_dtype, device=a_q.device)
+    fp8_block_scaled_gemm(a_q, a_scale, a_kind, b_q, b_scale, b_kind, y, stream)
+    return y
+
+
+def grouped_gemm(a_q, a_scale, a_kind, b_q, b_scale, b_kind, group_offsets, out_dtype=torch.bfloat16, stream=None):
+    y = torch.empty((a_q.shape[0], b_q.shape[1]), dtype=out_dtype, device=a_q.device)
+    fp8_grouped_gemm(a_q, a_scale, a_kind, b_q, b_scale, b_kind, group_offsets, y, stream)
+    return y

@@ -1,0 +1,152 @@
+// C-ABI entry points of the fp8blk library: argument validation, device
+// checks and kernel dispatch.  The declarations and their contracts are in
+// include/fp8blk.h.
+#include "fp8blk.h"
+
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <string.h>
+
+#include "launch.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+struct DeviceInfo {
+  bool ok = false;
+  bool supported = false;
+  int num_cu = 0;
+};
+
+DeviceInfo g_dev[kMaxDevices];
+std::once_flag g_once[kMaxDevices];
+
+// Properties of the current device, read once per device.
+int current_device(DeviceInfo** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FP8_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return FP8_ERR_UNSUPPORTED;
+  std::call_once(g_once[dev], [dev] {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return;
+    g_dev[dev].ok = true;
+    g_dev[dev].num_cu = prop.multiProcessorCount;
+    g_dev[dev].supported = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  });
+  if (!g_dev[dev].ok) return FP8_ERR_HIP;
+  if (!g_dev[dev].supported) return FP8_ERR_UNSUPPORTED;
+  *out = &g_dev[dev];
+  return FP8_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? FP8_OK : FP8_ERR_HIP; }
+
+bool valid_kind(int k) { return k == FP8_BLOCK_1x32_E8M0 || k == FP8_BLOCK_1x128_F32 || k == FP8_BLOCK_128x128_F32; }
+
+// Scale pointer alignment: fp32 scales 4 bytes; E8M0 bytes read four at a
+// time by the GEMMs, so 4 bytes there too (quantize writes single bytes).
+uintptr_t scale_align(int kind, bool gemm) { return kind == FP8_BLOCK_1x32_E8M0 ? (gemm ? 4 : 1) : 4; }
+
+}  // namespace
+
+extern "C" {
+
+int fp8_abi_version(void) { return FP8BLK_ABI_VERSION; }
+
+const char* fp8_status_string(int s) {
+  switch (s) {
+    case FP8_OK: return "ok";
+    case FP8_ERR_INVALID_ARG: return "invalid argument (null pointer, unknown enum or bad rank)";
+    case FP8_ERR_SHAPE: return "invalid shape (negative or not a multiple of the block)";
+    case FP8_ERR_ALIGN: return "pointer not aligned as required";
+    case FP8_ERR_UNSUPPORTED: return "unsupported block-kind combination or device (gfx950 required)";
+    case FP8_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int fp8_block_quantize(const uint16_t* x, int64_t rows, int64_t cols, int kind, int rule, uint8_t* q, void* scale,
+                       uint16_t* xdq, void* stream) {
+  if (!valid_kind(kind)) return FP8_ERR_INVALID_ARG;
+  if (kind == FP8_BLOCK_1x32_E8M0 && rule != FP8_E8M0_CEIL && rule != FP8_E8M0_FLOOR) return FP8_ERR_INVALID_ARG;
+  if (rows < 0 || cols < 0) return FP8_ERR_SHAPE;
+  const int64_t bc = kind == FP8_BLOCK_1x32_E8M0 ? 32 : 128;
+  if (cols % bc) return FP8_ERR_SHAPE;
+  if (kind == FP8_BLOCK_128x128_F32 && rows % 128) return FP8_ERR_SHAPE;
+  if (kind == FP8_BLOCK_128x128_F32 && rows / 128 > 65535) return FP8_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return FP8_OK;
+  if (!x || !q || !scale) return FP8_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(q, 16) || (xdq && !aligned(xdq, 16)) || !aligned(scale, scale_align(kind, false)))
+    return FP8_ERR_ALIGN;
+  DeviceInfo* dev = nullptr;
+  if (int s = current_device(&dev)) return s;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (kind == FP8_BLOCK_128x128_F32)
+    return hip_status(fp8blk::launch_quant_128(x, rows, cols, q, static_cast<float*>(scale), xdq, st));
+  return hip_status(fp8blk::launch_quant_rows(x, rows, cols, kind == FP8_BLOCK_1x32_E8M0 ? 32 : 128,
+                                              rule == FP8_E8M0_FLOOR, q, scale, xdq, dev->num_cu, st));
+}
+
+int fp8_fake_quant_merge(const uint16_t* w, const uint16_t* lora_b, const uint16_t* lora_a, int64_t n, int64_t k,
+                         int64_t r, uint8_t* q, float* scale, uint16_t* wdq, void* stream) {
+  if (r < 1 || r > 64) return FP8_ERR_INVALID_ARG;
+  if (n < 0 || k < 0 || n % 128 || k % 128 || n / 128 > 65535) return FP8_ERR_SHAPE;
+  if (n == 0 || k == 0) return FP8_OK;
+  if (!w || !lora_b || !lora_a || !q || !scale) return FP8_ERR_INVALID_ARG;
+  if (!aligned(w, 16) || !aligned(q, 16) || !aligned(scale, 4) || !aligned(lora_a, 4) || !aligned(lora_b, 2) ||
+      (wdq && !aligned(wdq, 16)))
+    return FP8_ERR_ALIGN;
+  DeviceInfo* dev = nullptr;
+  if (int s = current_device(&dev)) return s;
+  return hip_status(fp8blk::launch_merge(w, lora_b, lora_a, n, k, r, q, scale, wdq, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int fp8_block_scaled_gemm(const uint8_t* a_q, const void* a_scale, int a_kind, const uint8_t* b_q, const void* b_scale,
+                          int b_kind, int64_t m, int64_t n, int64_t k, void* y, int y_type, void* stream) {
+  if (!valid_kind(a_kind) || !valid_kind(b_kind)) return FP8_ERR_INVALID_ARG;
+  if (y_type != FP8_OUT_BF16 && y_type != FP8_OUT_F32) return FP8_ERR_INVALID_ARG;
+  const bool f32pair = a_kind == FP8_BLOCK_1x128_F32 && b_kind == FP8_BLOCK_128x128_F32;
+  const bool mxpair = a_kind == FP8_BLOCK_1x32_E8M0 && b_kind == FP8_BLOCK_1x32_E8M0;
+  if (!f32pair && !mxpair) return FP8_ERR_UNSUPPORTED;
+  if (m < 0 || n < 0 || k < 0 || n % 128 || k % 128) return FP8_ERR_SHAPE;
+  if ((m + 127) / 128 > 0x7FFFFFFF || n / 128 > 65535) return FP8_ERR_SHAPE;
+  if (m == 0 || n == 0) return FP8_OK;
+  if (!y) return FP8_ERR_INVALID_ARG;
+  if (k == 0) return FP8_ERR_SHAPE;  // an empty reduction is not a block-scaled product
+  if (!a_q || !b_q || !a_scale || !b_scale) return FP8_ERR_INVALID_ARG;
+  if (!aligned(a_q, 16) || !aligned(b_q, 16) || !aligned(a_scale, scale_align(a_kind, true)) ||
+      !aligned(b_scale, scale_align(b_kind, true)) || !aligned(y, y_type == FP8_OUT_F32 ? 4 : 2))
+    return FP8_ERR_ALIGN;
+  DeviceInfo* dev = nullptr;
+  if (int s = current_device(&dev)) return s;
+  return hip_status(fp8blk::launch_gemm(a_q, a_scale, a_kind, b_q, b_scale, b_kind, m, n, k, y,
+                                        y_type == FP8_OUT_F32, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int fp8_grouped_gemm(const uint8_t* a_q, const void* a_scale, int a_kind, const uint8_t* b_q, const void* b_scale,
+                     int b_kind, const int32_t* group_offsets, int64_t groups, int64_t total_m, int64_t n, int64_t k,
+                     void* y, int y_type, void* stream) {
+  if (!valid_kind(a_kind) || !valid_kind(b_kind)) return FP8_ERR_INVALID_ARG;
+  if (y_type != FP8_OUT_BF16 && y_type != FP8_OUT_F32) return FP8_ERR_INVALID_ARG;
+  if (a_kind != FP8_BLOCK_1x128_F32 || (b_kind != FP8_BLOCK_1x32_E8M0 && b_kind != FP8_BLOCK_128x128_F32))
+    return FP8_ERR_UNSUPPORTED;
+  if (groups < 1 || groups > 1024) return FP8_ERR_INVALID_ARG;
+  if (total_m < 0 || n < 0 || k <= 0 || n % 128 || k % 128) return FP8_ERR_SHAPE;
+  if (total_m / 128 + groups > 0x7FFFFFFF || n / 128 > 65535 || total_m > 0x7FFFFFFF) return FP8_ERR_SHAPE;
+  if (total_m == 0 || n == 0) return FP8_OK;
+  if (!a_q || !a_scale || !b_q || !b_scale || !group_offsets || !y) return FP8_ERR_INVALID_ARG;
+  if (!aligned(a_q, 16) || !aligned(b_q, 16) || !aligned(a_scale, 4) || !aligned(b_scale, 4) ||
+      !aligned(group_offsets, 4) || !aligned(y, y_type == FP8_OUT_F32 ? 4 : 2))
+    return FP8_ERR_ALIGN;
+  DeviceInfo* dev = nullptr;
+  if (int s = current_device(&dev)) return s;
+  return hip_status(fp8blk::launch_grouped_gemm(a_q, a_scale, a_kind, b_q, b_scale, b_kind, group_offsets, groups,
+                                                total_m, n, k, y, y_type == FP8_OUT_F32,
+                                                reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

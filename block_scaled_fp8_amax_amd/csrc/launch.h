@@ -1,0 +1,22 @@
+// Kernel launchers of the fp8blk library (internal; arguments are already
+// validated by abi.cpp).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8blk {
+
+hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, int blk, bool floor_rule, uint8_t* q,
+                             void* scale, uint16_t* xdq, int num_cu, hipStream_t stream);
+hipError_t launch_quant_128(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* q, float* scale, uint16_t* xdq,
+                            hipStream_t stream);
+hipError_t launch_merge(const uint16_t* w, const uint16_t* lb, const uint16_t* la, int64_t n, int64_t k, int64_t r,
+                        uint8_t* q, float* scale, uint16_t* wdq, hipStream_t stream);
+hipError_t launch_gemm(const uint8_t* a, const void* sa, int a_kind, const uint8_t* b, const void* sb, int b_kind,
+                       int64_t m, int64_t n, int64_t k, void* y, bool out_f32, hipStream_t stream);
+hipError_t launch_grouped_gemm(const uint8_t* a, const void* sa, int a_kind, const uint8_t* b, const void* sb,
+                               int b_kind, const int32_t* offsets, int64_t groups, int64_t total_m, int64_t n,
+                               int64_t k, void* y, bool out_f32, hipStream_t stream);
+
+}  // namespace fp8blk

@@ -1,0 +1,209 @@
+// Block-wise FP8 quantization kernels (gfx950).
+//
+// Method: per block amax -> scale -> round-to-nearest-even, saturating
+// e4m3fn encode ("DeepSeek-V3 Blog 5", "The Solution: Block-Wise
+// Quantization"; "FP8 в DeepSeek V3", 128x128 weight blocks with an fp32
+// scale inverse and per-token 1x128 activation groups; "fireworks-prequant
+// 0.1.0", MXFP8 1x32 blocks with E8M0 scales).
+//
+// Two kernels:
+//   quant_rows  : 1x32 and 1x128 blocks.  Both run along the contiguous
+//                 dimension and the column count is a multiple of the block,
+//                 so the matrix is a flat array of consecutive blocks and the
+//                 scale array is in block order.  One 16-byte load per lane
+//                 holds 8 bf16; a block is 4 (1x32) or 16 (1x128) adjacent
+//                 lanes, reduced with DPP lane permutations.  Each wave
+//                 streams U chunks per lane per iteration (4 KiB of bf16 in
+//                 flight per wave) over a grid-stride loop.
+//   quant_128   : 128x128 blocks, one 256-thread workgroup per block; every
+//                 thread keeps its 64 elements in registers between the amax
+//                 pass and the encode pass, so the block is read once.
+#include "device.h"
+#include "launch.h"
+
+namespace fp8blk {
+
+constexpr int kQRowsThreads = 256;
+constexpr int kQRowsU = 4;
+
+// Encode the 8 bf16 values of one chunk; returns the codes as two dwords and
+// (if DQ) writes the bf16 fake-quant values to dq[0..3].
+template <bool F32SCALE, bool FLOOR, bool DQ>
+__device__ __forceinline__ u32x2 encode_chunk(const u32x4& v, const F32Block& fb, float inv, float sval,
+                                              u32x4* dq) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  float f[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float lo = bf_lo(w[i]), hi = bf_hi(w[i]);
+    if constexpr (F32SCALE) {
+      f[2 * i] = f32_quot(lo, fb);
+      f[2 * i + 1] = f32_quot(hi, fb);
+    } else {
+      f[2 * i] = lo * inv;        // exact power-of-two scaling
+      f[2 * i + 1] = hi * inv;
+      if constexpr (FLOOR) {
+        f[2 * i] = clamp448(f[2 * i]);
+        f[2 * i + 1] = clamp448(f[2 * i + 1]);
+      }
+    }
+  }
+  u32x2 c;
+  c.x = cvt4_e4m3(f[0], f[1], f[2], f[3]);
+  c.y = cvt4_e4m3(f[4], f[5], f[6], f[7]);
+  if constexpr (DQ) {
+    float d[8];
+    decode4_e4m3(c.x, d);
+    decode4_e4m3(c.y, d + 4);
+    u32x4 o;
+    o.x = pack_bf16x2(d[0] * sval, d[1] * sval);
+    o.y = pack_bf16x2(d[2] * sval, d[3] * sval);
+    o.z = pack_bf16x2(d[4] * sval, d[5] * sval);
+    o.w = pack_bf16x2(d[6] * sval, d[7] * sval);
+    *dq = o;
+  }
+  return c;
+}
+
+// BLK = 32 (E8M0 scales) or 128 (fp32 scales).
+template <int BLK, bool FLOOR, bool DQ>
+__global__ __launch_bounds__(kQRowsThreads) void quant_rows_kernel(const u32x4* __restrict__ x, int64_t nchunks,
+                                                                   u32x2* __restrict__ q, void* __restrict__ scale,
+                                                                   u32x4* __restrict__ xdq) {
+  constexpr int LANES = BLK / 8;
+  constexpr bool F32SCALE = (BLK == 128);
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = (int64_t)blockIdx.x * (kQRowsThreads / 64) + (threadIdx.x >> 6);
+  const int64_t nwaves = (int64_t)gridDim.x * (kQRowsThreads / 64);
+  for (int64_t base = wave * 64 * kQRowsU; base < nchunks; base += nwaves * 64 * kQRowsU) {
+    u32x4 v[kQRowsU];
+#pragma unroll
+    for (int u = 0; u < kQRowsU; ++u) {
+      const int64_t idx = base + u * 64 + lane;
+      v[u] = idx < nchunks ? __builtin_nontemporal_load(x + idx) : (u32x4){0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < kQRowsU; ++u) {
+      const int64_t idx = base + u * 64 + lane;
+      const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+      const uint32_t amax = group_max<LANES>(absmax_bits<4>(w));
+      F32Block fb;
+      float inv = 0.f, sval;
+      uint32_t code = 0;
+      if constexpr (F32SCALE) {
+        fb = f32_block(amax);
+        sval = fb.s;
+      } else {
+        code = e8m0_code<FLOOR>(amax);
+        inv = e8m0_inv(code);
+        sval = e8m0_val(code);
+      }
+      u32x4 dqv;
+      const u32x2 c = encode_chunk<F32SCALE, FLOOR, DQ>(v[u], fb, inv, sval, &dqv);
+      if (idx < nchunks) {
+        __builtin_nontemporal_store(c, q + idx);
+        if constexpr (DQ) __builtin_nontemporal_store(dqv, xdq + idx);
+        if ((lane & (LANES - 1)) == 0) {
+          if constexpr (F32SCALE)
+            reinterpret_cast<float*>(scale)[idx / LANES] = fb.s;
+          else
+            reinterpret_cast<uint8_t*>(scale)[idx / LANES] = (uint8_t)code;
+        }
+      }
+    }
+  }
+}
+
+// 128x128 blocks: grid = (cols/128, rows/128), 256 threads.
+// Thread t covers column chunk (t % 16) * 8 of rows (t / 16) + 16 * i.
+template <bool DQ>
+__global__ __launch_bounds__(256) void quant_128_kernel(const uint16_t* __restrict__ x, int64_t cols,
+                                                        uint8_t* __restrict__ q, float* __restrict__ scale,
+                                                        uint16_t* __restrict__ xdq) {
+  __shared__ uint32_t red[4];
+  const int t = threadIdx.x;
+  const int64_t r0 = (int64_t)blockIdx.y * 128 + (t >> 4);
+  const int64_t c0 = (int64_t)blockIdx.x * 128 + (t & 15) * 8;
+  u32x4 v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + (r0 + 16 * i) * cols + c0));
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+    const uint32_t mi = absmax_bits<4>(w);
+    m = m > mi ? m : mi;
+  }
+  m = wave_max(m);
+  if ((t & 63) == 0) red[t >> 6] = m;
+  __syncthreads();
+  m = red[0];
+#pragma unroll
+  for (int i = 1; i < 4; ++i) m = m > red[i] ? m : red[i];
+  const F32Block fb = f32_block(m);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    u32x4 dqv;
+    const u32x2 c = encode_chunk<true, false, DQ>(v[i], fb, 0.f, fb.s, &dqv);
+    const int64_t off = (r0 + 16 * i) * cols + c0;
+    __builtin_nontemporal_store(c, reinterpret_cast<u32x2*>(q + off));
+    if constexpr (DQ) __builtin_nontemporal_store(dqv, reinterpret_cast<u32x4*>(xdq + off));
+  }
+  if (t == 0) scale[(int64_t)blockIdx.y * (cols / 128) + blockIdx.x] = fb.s;
+}
+
+// ------------------------------------------------------------------ launchers
+
+static int rows_grid(int64_t nchunks, int num_cu) {
+  const int64_t per_block = (int64_t)(kQRowsThreads / 64) * 64 * kQRowsU;  // chunks per workgroup pass
+  int64_t need = (nchunks + per_block - 1) / per_block;
+  const int64_t cap = (int64_t)num_cu * 8;
+  if (need > cap) need = cap;
+  if (need < 1) need = 1;
+  return (int)need;
+}
+
+hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, int blk, bool floor_rule, uint8_t* q,
+                             void* scale, uint16_t* xdq, int num_cu, hipStream_t stream) {
+  const int64_t nchunks = rows * cols / 8;
+  const int grid = rows_grid(nchunks, num_cu);
+  const u32x4* xv = reinterpret_cast<const u32x4*>(x);
+  u32x2* qv = reinterpret_cast<u32x2*>(q);
+  u32x4* dv = reinterpret_cast<u32x4*>(xdq);
+  if (blk == 128) {
+    if (xdq)
+      hipLaunchKernelGGL((quant_rows_kernel<128, false, true>), dim3(grid), dim3(kQRowsThreads), 0, stream, xv,
+                         nchunks, qv, scale, dv);
+    else
+      hipLaunchKernelGGL((quant_rows_kernel<128, false, false>), dim3(grid), dim3(kQRowsThreads), 0, stream, xv,
+                         nchunks, qv, scale, dv);
+  } else if (floor_rule) {
+    if (xdq)
+      hipLaunchKernelGGL((quant_rows_kernel<32, true, true>), dim3(grid), dim3(kQRowsThreads), 0, stream, xv,
+                         nchunks, qv, scale, dv);
+    else
+      hipLaunchKernelGGL((quant_rows_kernel<32, true, false>), dim3(grid), dim3(kQRowsThreads), 0, stream, xv,
+                         nchunks, qv, scale, dv);
+  } else {
+    if (xdq)
+      hipLaunchKernelGGL((quant_rows_kernel<32, false, true>), dim3(grid), dim3(kQRowsThreads), 0, stream, xv,
+                         nchunks, qv, scale, dv);
+    else
+      hipLaunchKernelGGL((quant_rows_kernel<32, false, false>), dim3(grid), dim3(kQRowsThreads), 0, stream, xv,
+                         nchunks, qv, scale, dv);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_128(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* q, float* scale, uint16_t* xdq,
+                            hipStream_t stream) {
+  dim3 grid((unsigned)(cols / 128), (unsigned)(rows / 128));
+  if (xdq)
+    hipLaunchKernelGGL((quant_128_kernel<true>), grid, dim3(256), 0, stream, x, cols, q, scale, xdq);
+  else
+    hipLaunchKernelGGL((quant_128_kernel<false>), grid, dim3(256), 0, stream, x, cols, q, scale, xdq);
+  return hipGetLastError();
+}
+
+}  // namespace fp8blk

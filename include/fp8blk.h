@@ -1,0 +1,190 @@
+/*
+ * fp8blk -- fine-grained block-scaled FP8 quantization and block-scaled FP8
+ * GEMM for AMD Instinct MI355X (gfx950).  C ABI.
+ *
+ * Pages cited (titles as published):
+ *   [Fireworks-QAT] "DeepSeek R1 and V3 get quantization-aware fine-tuning on
+ *                   Fireworks, keeping FP8 serving without the accuracy drop",
+ *                   sections Synopsis and Interpretation.
+ *   [DSV3-Blog5]    "DeepSeek-V3 Blog 5: Low-Precision Training - The FP8
+ *                   Revolution in Large-Scale AI", sections "The Solution:
+ *                   Block-Wise Quantization" and "Hardware Optimization:
+ *                   Leveraging NVIDIA Tensor Cores for FP8".
+ *   [FP8-DSV3-ru]   "FP8 в DeepSeek V3: как низкая точность ускоряет обучение
+ *                   и инференс", sections "Как FP8 встроен в DeepSeek V3",
+ *                   "Почему обычное округление не подходит", "Инференс с FP8",
+ *                   "Почему FP8 требует scale factors".
+ *   [prequant]      "fireworks-prequant 0.1.0", sections "Quick start" and
+ *                   "Formats" (MXFP8: 1x32 blocks, E8M0 scales; the
+ *                   routed-expert rule).
+ *
+ * Conventions shared by every entry point
+ *   - Tensor pointers are DEVICE pointers (memory of the current HIP device)
+ *     holding dense row-major matrices; the last index is contiguous.  bf16
+ *     travels as uint16_t bit patterns, FP8 e4m3fn codes as uint8_t.
+ *   - The caller allocates and owns every buffer; the library allocates
+ *     nothing, keeps no per-call state and never synchronizes.  Work is
+ *     enqueued on `stream` (a hipStream_t passed as void*, NULL = the
+ *     default stream) and runs asynchronously.
+ *   - Arguments are validated on the host before anything is enqueued; a
+ *     nonzero fp8_status is returned and nothing is launched.  A launch
+ *     failure reported by the runtime returns FP8_ERR_HIP.  Device-side
+ *     faults caused by invalid pointers are not detectable here.
+ *   - Matrices with zero rows or columns are valid and enqueue nothing.
+ *   - Inputs must be finite (no Inf/NaN in bf16 data).
+ *   - Results are deterministic: identical bytes for identical inputs,
+ *     independent of stream and repetition.
+ *   - The device must be gfx950 (MI355X/MI350X); other devices get
+ *     FP8_ERR_UNSUPPORTED.
+ */
+#ifndef FP8BLK_H
+#define FP8BLK_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP8BLK_ABI_VERSION 1
+
+typedef enum {
+  FP8_OK = 0,
+  FP8_ERR_INVALID_ARG = 1, /* null pointer, unknown enum, bad rank          */
+  FP8_ERR_SHAPE = 2,       /* negative or non-divisible dimension            */
+  FP8_ERR_ALIGN = 3,       /* pointer not aligned as documented              */
+  FP8_ERR_UNSUPPORTED = 4, /* block-kind combination or device not handled   */
+  FP8_ERR_HIP = 5          /* the HIP runtime reported an error              */
+} fp8_status;
+
+/* Block geometry and scale type ([DSV3-Blog5] block-wise quantization;
+ * [FP8-DSV3-ru]: 128x128 weight blocks with an fp32 scale inverse and
+ * per-token 1x128 activation groups; [prequant]: MXFP8 = 1x32, E8M0). */
+typedef enum {
+  FP8_BLOCK_1x32_E8M0 = 0,   /* scale: uint8 E8M0 code, [rows][cols/32]        */
+  FP8_BLOCK_1x128_F32 = 1,   /* scale: float, [rows][cols/128]                 */
+  FP8_BLOCK_128x128_F32 = 2  /* scale: float, [rows/128][cols/128]             */
+} fp8_block;
+
+/* E8M0 exponent rule (the pages do not fix it).
+ * CEIL : X = smallest integer with amax <= 448 * 2^X (no element saturates).
+ * FLOOR: X = floor(log2 amax) - 8 (OCP MX rule; elements above 448*2^X
+ *        saturate to +-448).  Both clamp X to [-127, 127]; amax == 0 gives
+ *        X = -127.  The stored code is X + 127. */
+typedef enum { FP8_E8M0_CEIL = 0, FP8_E8M0_FLOOR = 1 } fp8_e8m0_rule;
+
+/* GEMM output element type. */
+typedef enum { FP8_OUT_BF16 = 0, FP8_OUT_F32 = 1 } fp8_out;
+
+/*
+ * fp8_block_quantize -- block-wise FP8 quantization of a bf16 matrix.
+ *
+ * Defined by: [DSV3-Blog5] "The Solution: Block-Wise Quantization" (each
+ * sub-matrix gets its own scaling factor); [FP8-DSV3-ru] "Почему обычное
+ * округление не подходит" (128x128 weight blocks, scale inverse for
+ * dequantization) and "Как FP8 встроен в DeepSeek V3" (online per-token,
+ * per-128-channel activation quantization); [prequant] "Quick start" and
+ * "Formats" (float8_e4m3fn weight + uint8 E8M0 weight_scale_inv, 1x32).
+ *
+ * For each block: amax = max |x|.
+ *   fp32 kinds: s = RN32(amax / 448) is stored; q = e4m3(RN32(x / s));
+ *               an all-zero block stores s = 0 and codes +-0.
+ *   E8M0 kind : X from `rule`; code X + 127 is stored; q = e4m3(x * 2^-X).
+ * e4m3(v): round to nearest even, saturate to +-448, keep the sign of zero.
+ *
+ * x     [rows x cols] bf16 (16-byte aligned).
+ * q     [rows x cols] e4m3fn codes out (16-byte aligned).
+ * scale out: uint8 [rows][cols/32] (1x32), float [rows][cols/128] (1x128,
+ *       4-byte aligned), float [rows/128][cols/128] (128x128, 4-byte aligned).
+ * xdq   optional (NULL = not written) [rows x cols] bf16 fake-quant output
+ *       RN_bf16(RN32(decode(q) * scale)), 16-byte aligned.
+ * rule  used by FP8_BLOCK_1x32_E8M0 only (ignored otherwise).
+ * Shape: rows, cols >= 0; cols % 32 == 0 (1x32) or cols % 128 == 0;
+ *        rows % 128 == 0 for 128x128.
+ */
+int fp8_block_quantize(const uint16_t* x, int64_t rows, int64_t cols, int kind, int rule,
+                       uint8_t* q, void* scale, uint16_t* xdq, void* stream);
+
+/*
+ * fp8_fake_quant_merge -- QAT forward of a LoRA-adapted weight: merge
+ * W + B.A in bf16, then fake-quantize the merged weight in 128x128 blocks.
+ *
+ * Defined by: [Fireworks-QAT] Synopsis and Interpretation (merged weights
+ * are fake-quantized in the forward pass; LoRA factors stay bf16; merged
+ * bf16 weights are converted to block-wise FP8 for serving); the 128x128
+ * block with fp32 scale from [FP8-DSV3-ru].
+ *
+ *   acc = 0; for r = 0..R-1: acc = RN32(acc + B[n,r] * A[r,k])
+ *   W'[n,k] = RN_bf16(RN32(W[n,k] + RN_bf16(acc)))
+ * then exactly fp8_block_quantize(W', n, k, FP8_BLOCK_128x128_F32, ...).
+ * W' itself is never written to memory.
+ *
+ * w      [n x k] bf16, lora_b [n x r] bf16, lora_a [r x k] bf16
+ *        (w 16-byte aligned; lora_b, lora_a 4-byte aligned).
+ * q      [n x k] codes out; scale float [n/128][k/128] out;
+ * wdq    optional [n x k] bf16 fake-quant output (NULL = not written).
+ * Shape: n % 128 == 0, k % 128 == 0, 1 <= r <= 64.
+ */
+int fp8_fake_quant_merge(const uint16_t* w, const uint16_t* lora_b, const uint16_t* lora_a,
+                         int64_t n, int64_t k, int64_t r, uint8_t* q, float* scale,
+                         uint16_t* wdq, void* stream);
+
+/*
+ * fp8_block_scaled_gemm -- Y = deq(A) . deq(B)^T with fp32 accumulation.
+ *
+ * Defined by: [DSV3-Blog5] "Hardware Optimization" (FP8 products on the
+ * matrix units, intermediate results promoted to higher precision before
+ * the final accumulation); [FP8-DSV3-ru] "Инференс с FP8" (FP8 matrix
+ * multiplication on block-quantized operands).
+ *
+ * a_q [m x k] codes with a_scale; b_q [n x k] codes with b_scale (both
+ * K-contiguous, as produced by fp8_block_quantize; 16-byte aligned).
+ * Supported (a_kind, b_kind):
+ *   (FP8_BLOCK_1x128_F32, FP8_BLOCK_128x128_F32): per 128-wide K chunk the
+ *        FP8 partial product is formed on the matrix cores and added to the
+ *        fp32 accumulator times sa[m][kb] * sb[n/128][kb];
+ *   (FP8_BLOCK_1x32_E8M0, FP8_BLOCK_1x32_E8M0): MXFP8 x MXFP8, the
+ *        power-of-two scales are applied inside the scaled matrix
+ *        instruction and accumulation is continuous in fp32.
+ * y      [m x n] out, bf16 (RN_bf16 of the fp32 result) or float, per y_type.
+ * Shape: m >= 0 (any), n % 128 == 0, k % 128 == 0.
+ */
+int fp8_block_scaled_gemm(const uint8_t* a_q, const void* a_scale, int a_kind,
+                          const uint8_t* b_q, const void* b_scale, int b_kind,
+                          int64_t m, int64_t n, int64_t k, void* y, int y_type, void* stream);
+
+/*
+ * fp8_grouped_gemm -- variable-M grouped GEMM over routed MoE experts.
+ *
+ * Defined by: the routed expert projections of [prequant] (MXFP8 weights,
+ * "Formats" and the routed-expert rule) and the FP8 MoE activations of
+ * [DSV3-Blog5] "Reducing Communication Overhead in MoE with FP8".
+ *
+ * Group g owns rows [off[g], off[g+1]) of A and expert matrix B[g]:
+ *   Y[rows of g] = deq(A[rows of g]) . deq(B[g])^T, fp32 accumulation.
+ * a_q [total_m x k] codes, a_kind = FP8_BLOCK_1x128_F32 (per-token scales
+ *     float [total_m][k/128]);
+ * b_q [groups x n x k] codes, b_kind = FP8_BLOCK_1x32_E8M0 (uint8
+ *     [groups][n][k/32]) or FP8_BLOCK_128x128_F32 (float
+ *     [groups][n/128][k/128]);
+ * group_offsets: DEVICE int32 [groups+1], off[0] = 0, non-decreasing,
+ *     off[groups] = total_m (not checked: a violation is undefined);
+ * y [total_m x n] out, bf16 or float per y_type.
+ * Shape: groups >= 1, total_m >= 0, n % 128 == 0, k % 128 == 0.
+ */
+int fp8_grouped_gemm(const uint8_t* a_q, const void* a_scale, int a_kind,
+                     const uint8_t* b_q, const void* b_scale, int b_kind,
+                     const int32_t* group_offsets, int64_t groups, int64_t total_m,
+                     int64_t n, int64_t k, void* y, int y_type, void* stream);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char* fp8_status_string(int status);
+
+/* FP8BLK_ABI_VERSION of the loaded library. */
+int fp8_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8BLK_H */

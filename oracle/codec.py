@@ -15,7 +15,8 @@ Rounding readings (none is printed on the pages):
     mantissa; magnitudes >= 448 saturate to 448 (0x7E); the sign bit is kept,
     so -0 and negative values that round to zero give 0x80.
   * fp32 -> bf16: IEEE round to nearest, ties to even.
-Inputs are required to be finite.
+Inputs to the FP8 encoder must be finite; the bf16 rounding follows IEEE
+overflow (values past the largest bf16 round to infinity).
 """
 
 import numpy as np
@@ -98,20 +99,26 @@ def f32_to_bf16(x):
     Plain form: the magnitude's two bf16 neighbours are the truncation t
     (drop the low 16 bits) and t + 1 ulp; the nearer one wins and a tie
     goes to the one with an even last bit.  Both distances are exact in
-    float64.  Inputs must be finite.
+    float64.  Above the largest finite bf16 the upper neighbour is 2^128,
+    i.e. infinity, as in IEEE overflow under round-to-nearest; +-inf maps to
+    +-inf.  NaN is rejected.
     """
     x = np.asarray(x, dtype=np.float32)
-    if not np.all(np.isfinite(x)):
-        raise ValueError("f32_to_bf16: inputs must be finite")
+    if np.any(np.isnan(x)):
+        raise ValueError("f32_to_bf16: NaN input")
     bits = x.view(np.uint32)
     sign = (bits >> np.uint32(31)).astype(np.uint32)
     mag_bits = bits & np.uint32(0x7FFFFFFF)
+    is_inf = mag_bits == np.uint32(0x7F800000)
+    mag_bits = np.where(is_inf, np.uint32(0), mag_bits)
     t = mag_bits >> np.uint32(16)                 # truncated bf16 magnitude
     lo = (t << np.uint32(16)).view(np.float32).astype(np.float64)
     up = ((t + np.uint32(1)) << np.uint32(16)).view(np.float32).astype(np.float64)
+    up = np.where(t + np.uint32(1) == np.uint32(0x7F80), 2.0 ** 128, up)
     a = mag_bits.view(np.float32).astype(np.float64)
     d_lo = a - lo
     d_up = up - a
     take_up = (d_up < d_lo) | ((d_up == d_lo) & ((t & np.uint32(1)) == 1))
     r = np.where(take_up, t + np.uint32(1), t)
+    r = np.where(is_inf, np.uint32(0x7F80), r)
     return (r | (sign << np.uint32(15))).astype(np.uint16)

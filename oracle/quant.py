@@ -142,10 +142,15 @@ def scale_multiplier(scale, kind, rows, cols):
 
 
 def dequantize_f32(q, scale, kind):
-    """RN32(decode(q) * scale) as float32 [R, C] (the dequantized operand)."""
+    """RN32(decode(q) * scale) as float32 [R, C] (the dequantized operand).
+
+    IEEE float32 multiply: a product beyond the largest float rounds to
+    +-inf (possible only for E8M0 blocks whose amax is within one e4m3 step
+    of the bf16 maximum)."""
     rows, cols = q.shape
     dq = e4m3_decode(q).astype(np.float32)           # exact
-    return (dq * scale_multiplier(scale, kind, rows, cols)).astype(np.float32)
+    with np.errstate(over="ignore"):
+        return (dq * scale_multiplier(scale, kind, rows, cols)).astype(np.float32)
 
 
 def dequantize(q, scale, kind):

@@ -1,0 +1,112 @@
+"""Host-side checks of the C-ABI library (no GPU needed).
+
+The library loads, exports every function include/fp8blk.h declares, and
+its argument validation returns the documented status codes before any
+device work (the checks below never reach a kernel launch).
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_scaled_fp8_amax_amd as fb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8blk.h")
+
+OK, INVALID, SHAPE, ALIGN, UNSUP, HIPERR = 0, 1, 2, 3, 4, 5
+A16 = 0x10000          # a fake, 16-byte aligned address (never dereferenced)
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(fp8_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fb.library_path):
+        pytest.fail("libfp8blk.so is not built (run __graft_entry__.build())")
+    return fb.library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared_functions()
+    assert set(names) == {"fp8_block_quantize", "fp8_fake_quant_merge", "fp8_block_scaled_gemm",
+                          "fp8_grouped_gemm", "fp8_status_string", "fp8_abi_version"}
+    raw = ctypes.CDLL(fb.library_path)
+    for n in names:
+        assert hasattr(raw, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert lib.fp8_abi_version() == 1
+    for s in range(6):
+        assert len(lib.fp8_status_string(s)) > 0
+    assert lib.fp8_status_string(99) == b"unknown status"
+
+
+def test_quantize_validation(lib):
+    q = lib.fp8_block_quantize
+    assert q(A16, 4, 64, 7, 0, A16, A16, None, None) == INVALID           # unknown kind
+    assert q(A16, 4, 64, 0, 5, A16, A16, None, None) == INVALID           # unknown rule (1x32)
+    assert q(A16, 4, 48, 0, 0, A16, A16, None, None) == SHAPE             # 48 % 32
+    assert q(A16, 4, 64, 1, 0, A16, A16, None, None) == SHAPE             # 64 % 128
+    assert q(A16, 64, 128, 2, 0, A16, A16, None, None) == SHAPE           # rows % 128
+    assert q(A16, -1, 128, 1, 0, A16, A16, None, None) == SHAPE
+    assert q(None, 0, 128, 1, 0, None, None, None, None) == OK            # empty: nothing to do
+    assert q(None, 4, 0, 0, 0, None, None, None, None) == OK
+    assert q(None, 4, 128, 1, 0, A16, A16, None, None) == INVALID         # null input
+    assert q(A16 + 8, 4, 128, 1, 0, A16, A16, None, None) == ALIGN        # x not 16-B aligned
+    assert q(A16, 4, 128, 1, 0, A16, A16 + 2, None, None) == ALIGN        # fp32 scale not 4-B aligned
+    assert q(A16, 4, 128, 1, 0, A16, A16, A16 + 4, None) == ALIGN         # xdq not 16-B aligned
+
+
+def test_merge_validation(lib):
+    m = lib.fp8_fake_quant_merge
+    assert m(A16, A16, A16, 128, 128, 0, A16, A16, None, None) == INVALID    # rank 0
+    assert m(A16, A16, A16, 128, 128, 65, A16, A16, None, None) == INVALID   # rank > 64
+    assert m(A16, A16, A16, 100, 128, 16, A16, A16, None, None) == SHAPE
+    assert m(A16, A16, A16, 0, 128, 16, A16, A16, None, None) == OK
+    assert m(A16, None, A16, 128, 128, 16, A16, A16, None, None) == INVALID
+    assert m(A16 + 2, A16, A16, 128, 128, 16, A16, A16, None, None) == ALIGN
+
+
+def test_gemm_validation(lib):
+    g = lib.fp8_block_scaled_gemm
+    assert g(A16, A16, 1, A16, A16, 1, 8, 128, 128, A16, 0, None) == UNSUP       # (1x128, 1x128)
+    assert g(A16, A16, 0, A16, A16, 2, 8, 128, 128, A16, 0, None) == UNSUP
+    assert g(A16, A16, 9, A16, A16, 2, 8, 128, 128, A16, 0, None) == INVALID
+    assert g(A16, A16, 1, A16, A16, 2, 8, 128, 128, A16, 3, None) == INVALID     # bad out type
+    assert g(A16, A16, 1, A16, A16, 2, 8, 100, 128, A16, 0, None) == SHAPE
+    assert g(A16, A16, 1, A16, A16, 2, 8, 128, 96, A16, 0, None) == SHAPE
+    assert g(A16, A16, 1, A16, A16, 2, 0, 128, 128, None, 0, None) == OK         # m = 0
+    assert g(A16, A16, 1, A16, A16, 2, 8, 128, 0, A16, 0, None) == SHAPE         # empty reduction
+    assert g(A16 + 1, A16, 1, A16, A16, 2, 8, 128, 128, A16, 0, None) == ALIGN
+    assert g(A16, A16, 0, A16, A16 + 1, 0, 8, 128, 128, A16, 0, None) == ALIGN    # E8M0 scales: 4 B
+    assert g(A16, A16, 1, A16, A16, 2, 8, 128, 128, A16 + 2, 1, None) == ALIGN    # f32 out: 4 B
+
+
+def test_grouped_validation(lib):
+    g = lib.fp8_grouped_gemm
+    assert g(A16, A16, 1, A16, A16, 0, A16, 0, 8, 128, 128, A16, 0, None) == INVALID     # no groups
+    assert g(A16, A16, 1, A16, A16, 0, A16, 1025, 8, 128, 128, A16, 0, None) == INVALID  # too many
+    assert g(A16, A16, 0, A16, A16, 0, A16, 4, 8, 128, 128, A16, 0, None) == UNSUP       # A must be 1x128
+    assert g(A16, A16, 1, A16, A16, 1, A16, 4, 8, 128, 128, A16, 0, None) == UNSUP       # B 1x128
+    assert g(A16, A16, 1, A16, A16, 0, A16, 4, 8, 130, 128, A16, 0, None) == SHAPE
+    assert g(A16, A16, 1, A16, A16, 0, A16, 4, 0, 128, 128, A16, 0, None) == OK          # no rows
+    assert g(A16, A16, 1, A16, A16, 0, None, 4, 8, 128, 128, A16, 0, None) == INVALID
+    assert g(A16, A16, 1, A16, A16, 0, A16 + 2, 4, 8, 128, 128, A16, 0, None) == ALIGN
+
+
+def test_python_binding_raises_with_status(lib):
+    import torch
+    x = torch.zeros((4, 48), dtype=torch.bfloat16)
+    q = torch.zeros((4, 48), dtype=torch.uint8)
+    s = torch.zeros((4, 1), dtype=torch.uint8)
+    with pytest.raises(fb.Fp8Error) as ei:
+        fb.fp8_block_quantize(x, "1x32", "ceil", q, s)
+    assert ei.value.status == SHAPE

@@ -1,0 +1,178 @@
+"""GPU parity of fp8_block_quantize against the oracle (bit-exact).
+
+Codes, scales and fake-quant outputs must equal the oracle's bytes.  Cases:
+shapes spanning several blocks and ragged row counts, every block kind and
+E8M0 rule, an exhaustive-per-mantissa domain sweep of (x, amax) pairs, the
+degenerate blocks (all zero, signed zeros, subnormal and huge amax), the
+full-size activation/weight shapes of the dense and QAT projections, and
+determinism across repetitions and launch geometries.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import codec, quant
+from tests.gpu_helpers import assert_bytes_equal, bf16_from_bits, run_quantize
+from workloads import bf16_bits, dense_projection, mx_small, qat_forward
+
+pytestmark = pytest.mark.gpu
+
+KINDS = [("1x32", "ceil"), ("1x32", "floor"), ("1x128", "ceil"), ("128x128", "ceil")]
+
+
+def _check(xbits, kind, rule, dequant=True):
+    print(f"[quantize] kind={kind} rule={rule} shape={xbits.shape}", flush=True)
+    q, s, xdq = run_quantize(bf16_from_bits(xbits), kind, rule, dequant)
+    oq, os_, oxdq = quant.quantize(xbits, kind, rule)
+    assert_bytes_equal(q, oq, f"{kind}/{rule} codes")
+    assert_bytes_equal(s, os_, f"{kind}/{rule} scales")
+    if dequant:
+        assert_bytes_equal(xdq, oxdq, f"{kind}/{rule} dequant")
+
+
+def _random_bits(rows, cols, seed, spread=True):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((rows, cols)).astype(np.float32)
+    if spread:
+        x *= np.exp2(rng.uniform(-40, 40, size=(rows, 1))).astype(np.float32)
+        idx = rng.choice(x.size, x.size // 500, replace=False)
+        x.ravel()[idx] *= 100
+    return codec.f32_to_bf16(x)
+
+
+@pytest.mark.parametrize("kind,rule", KINDS)
+@pytest.mark.parametrize("shape", [(128, 128), (384, 640), (1, 128), (3, 4096), (1024, 384)])
+def test_random_shapes(kind, rule, shape):
+    rows, cols = shape
+    if kind == "128x128" and rows % 128:
+        pytest.skip("128x128 needs rows % 128 == 0")
+    _check(_random_bits(rows, cols, seed=rows * 7 + cols), kind, rule)
+
+
+@pytest.mark.parametrize("kind,rule", [("1x32", "ceil"), ("1x128", "ceil")])
+def test_ragged_rows_and_tail(kind, rule):
+    # row counts that leave a partial final wave-tile in the streaming kernel
+    for rows in (5, 33, 257, 1001):
+        _check(_random_bits(rows, 256, seed=rows), kind, rule)
+
+
+def test_codes_only_variant_matches():
+    xb = _random_bits(256, 512, seed=3)
+    for kind, rule in KINDS:
+        _check(xb, kind, rule, dequant=False)
+
+
+def test_degenerate_blocks():
+    rows, cols = 128, 256
+    x = np.zeros((rows, cols), np.uint16)
+    x[0, 1] = 0x8000                        # -0 in an all-zero block
+    x[1, :128] = 0x0001                     # least subnormal everywhere
+    x[1, 5] = 0x8001
+    x[2, :] = 0x7F7F                        # largest finite bf16
+    x[2, 7] = 0xFF7F
+    x[3, :] = 0x3F80                        # constant block
+    x[4, ::2] = 0x0080                      # least normal, half zeros
+    x[5, 64] = 0x1E00                       # amax ~ 2^-67 (pre-scaled path)
+    x[5, 65] = 0x1100
+    x[6, 0] = 0x2180                        # amax ~ 2^-60 boundary
+    x[6, 1:40] = np.arange(0x0100, 0x0100 + 39, dtype=np.uint16)
+    for kind, rule in KINDS:
+        _check(x, kind, rule)
+
+
+def _domain_blocks(amax_bits, blk):
+    """Rows of one block each: [amax, x_1, ..., x_{blk-1}] covering every
+    bf16 x with |x| <= amax, both signs."""
+    out = []
+    for ab in amax_bits:
+        xs = np.arange(0, ab + 1, dtype=np.uint32).astype(np.uint16)
+        xs = np.concatenate([xs, xs | 0x8000])
+        per = blk - 1
+        pad = (-len(xs)) % per
+        xs = np.concatenate([xs, np.zeros(pad, np.uint16)]).reshape(-1, per)
+        blocks = np.concatenate([np.full((len(xs), 1), ab, np.uint16), xs], axis=1)
+        out.append(blocks)
+    return np.concatenate(out)
+
+
+def test_domain_fp32_scale():
+    """Every bf16 x against 200 amax values: all 128 mantissas of one binade,
+    the extreme binades and the 2^-60 pre-scale boundary."""
+    rng = np.random.default_rng(12)
+    amax = list(range(0x3F80, 0x4000))                         # [1, 2): every mantissa
+    amax += [0x0001, 0x0040, 0x007F, 0x0080, 0x1D7F, 0x1D80, 0x1D81, 0x2180, 0x7F7F, 0x7F00]
+    amax += list(rng.integers(0x0001, 0x7F80, 62))
+    blocks = _domain_blocks(np.array(amax, dtype=np.uint32), 128)
+    _check(blocks, "1x128", "ceil")
+
+
+def test_domain_e8m0_every_exponent():
+    """For every E8M0 code: a block whose amax sets that code, with every bf16
+    magnitude up to amax (subsampled 1 in 3) and both signs."""
+    amax = []
+    for e in range(1, 255):
+        amax.append((e << 7) | 0x60)      # 1.75 * 2^(e-127): ceil code e-8
+        amax.append((e << 7) | 0x61)
+    blocks = []
+    for ab in amax:
+        xs = np.arange(0, ab + 1, 3, dtype=np.uint32).astype(np.uint16)
+        xs = np.concatenate([xs, xs | 0x8000])
+        pad = (-len(xs)) % 31
+        xs = np.concatenate([xs, np.zeros(pad, np.uint16)]).reshape(-1, 31)
+        blocks.append(np.concatenate([np.full((len(xs), 1), ab, np.uint16), xs], axis=1))
+    x = np.concatenate(blocks)
+    _check(x, "1x32", "ceil")
+    _check(x, "1x32", "floor")
+
+
+def test_mx_small_config():
+    d = mx_small("cuda")
+    for name in ("w", "x"):
+        _check(bf16_bits(d[name]), "1x32", "ceil")
+
+
+def test_dense_projection_full_size():
+    d = dense_projection("cuda")
+    x = d["x"]
+    print("[quantize] dense projection X 4096x7168 1x128 (sampled rows) + W 2048x7168 128x128", flush=True)
+    q, s, xdq = run_quantize(x, "1x128")
+    rows = np.random.default_rng(0).choice(x.shape[0], 256, replace=False)
+    xb = bf16_bits(x)[rows]
+    oq, os_, oxdq = quant.quantize(xb, "1x128")
+    assert_bytes_equal(q[rows], oq, "X codes")
+    assert_bytes_equal(s[rows], os_, "X scales")
+    assert_bytes_equal(xdq[rows], oxdq, "X dequant")
+    w = d["w"]
+    q, s, xdq = run_quantize(w, "128x128")
+    oq, os_, oxdq = quant.quantize(bf16_bits(w), "128x128")
+    assert_bytes_equal(q, oq, "W codes")
+    assert_bytes_equal(s, os_, "W scales")
+    assert_bytes_equal(xdq, oxdq, "W dequant")
+
+
+def test_qat_activations_full_size_sampled():
+    d = qat_forward("cuda")
+    x = d["x"]
+    print("[quantize] QAT X 8192x7168 1x128 (sampled rows)", flush=True)
+    q, s, xdq = run_quantize(x, "1x128")
+    rows = np.random.default_rng(1).choice(x.shape[0], 256, replace=False)
+    oq, os_, oxdq = quant.quantize(bf16_bits(x)[rows], "1x128")
+    assert_bytes_equal(q[rows], oq, "codes")
+    assert_bytes_equal(s[rows], os_, "scales")
+    assert_bytes_equal(xdq[rows], oxdq, "dequant")
+
+
+def test_determinism_and_geometry():
+    """Identical bytes over repetitions and when the matrix is quantized as a
+    whole or as separate row slices (different grids)."""
+    xb = _random_bits(4096, 1024, seed=21)
+    x = bf16_from_bits(xb)
+    for kind, rule in KINDS:
+        a = run_quantize(x, kind, rule)
+        b = run_quantize(x, kind, rule)
+        for u, v in zip(a, b):
+            assert np.array_equal(u, v)
+        parts = [run_quantize(x[i:i + 1024].contiguous(), kind, rule) for i in range(0, 4096, 1024)]
+        assert np.array_equal(np.concatenate([p[0] for p in parts]), a[0])
+        assert np.array_equal(np.concatenate([p[2] for p in parts]), a[2])

@@ -197,6 +197,19 @@ def test_bf16_round_matches_torch():
     assert np.array_equal(ours, theirs)
 
 
+def test_bf16_round_overflow_and_inf_match_torch():
+    """Beyond the largest finite bf16 (0x7F7F) the upper neighbour is inf:
+    the midpoint 0x7F7F8000 ties to even (inf), values below it stay finite."""
+    v = _f32(np.array([0x7F7F7FFF, 0x7F7F8000, 0x7F7F8001, 0x7F7FFFFF, 0x7F800000,
+                       0xFF7F7FFF, 0xFF7F8000, 0xFF800000], dtype=np.uint32))
+    ours = codec.f32_to_bf16(v)
+    theirs = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, theirs)
+    assert ours.tolist() == [0x7F7F, 0x7F80, 0x7F80, 0x7F80, 0x7F80, 0xFF7F, 0xFF80, 0xFF80]
+    with pytest.raises(ValueError):
+        codec.f32_to_bf16(np.float32([np.nan]))
+
+
 def test_bf16_round_tie_examples():
     # 1 + 2^-8 is halfway between 1 and 1 + 2^-7: tie -> even (1.0)
     assert codec.f32_to_bf16(np.float32(1 + 2.0 ** -8)) == 0x3F80

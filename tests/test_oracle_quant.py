@@ -276,6 +276,21 @@ def test_128x128_bruteforce_one_block():
         assert int(q[i, j]) == want
 
 
+def test_dequant_overflow_of_e8m0_block_near_bf16_max():
+    """amax = 0x7F7F (3.39e38): X = 120 and 255*2^-... rounds up to the e4m3
+    value 256, so decode(q) * 2^120 = 2^128 overflows float32 to inf; the
+    fake-quant output is then bf16 inf, as IEEE rounding prescribes."""
+    x = np.zeros((1, 32), np.uint16)
+    x[0, 0] = 0x7F7F
+    x[0, 1] = 0xFF7F
+    q, s, xdq = quant.quantize(x, "1x32", "ceil")
+    assert int(s[0, 0]) == 247 and int(q[0, 0]) == 0x78 and int(q[0, 1]) == 0xF8
+    assert int(xdq[0, 0]) == 0x7F80 and int(xdq[0, 1]) == 0xFF80
+    ref = (torch.from_numpy(q).view(torch.float8_e4m3fn).float()
+           * torch.from_numpy(s).view(torch.float8_e8m0fnu).float().repeat_interleave(32, 1)).to(torch.bfloat16)
+    assert np.array_equal(xdq, ref.view(torch.int16).numpy().view(np.uint16))
+
+
 def test_shape_errors():
     with pytest.raises(ValueError):
         quant.quantize(np.zeros((4, 48), np.uint16), "1x32")
