@@ -113,13 +113,13 @@ int fp8_block_scaled_gemm(const uint8_t* a_q, const void* a_scale, int a_kind, c
   const bool mxpair = a_kind == FP8_BLOCK_1x32_E8M0 && b_kind == FP8_BLOCK_1x32_E8M0;
   if (!f32pair && !mxpair) return FP8_ERR_UNSUPPORTED;
   if (m < 0 || n < 0 || k < 0 || n % 128 || k % 128) return FP8_ERR_SHAPE;
-  if ((m + 127) / 128 > 0x7FFFFFFF || n / 128 > 65535) return FP8_ERR_SHAPE;
+  if ((m + 255) / 256 * (n / 128) > 0x7FFFFFFF) return FP8_ERR_SHAPE;
   if (m == 0 || n == 0) return FP8_OK;
   if (!y) return FP8_ERR_INVALID_ARG;
   if (k == 0) return FP8_ERR_SHAPE;  // an empty reduction is not a block-scaled product
   if (!a_q || !b_q || !a_scale || !b_scale) return FP8_ERR_INVALID_ARG;
   if (!aligned(a_q, 16) || !aligned(b_q, 16) || !aligned(a_scale, scale_align(a_kind, true)) ||
-      !aligned(b_scale, scale_align(b_kind, true)) || !aligned(y, y_type == FP8_OUT_F32 ? 4 : 2))
+      !aligned(b_scale, scale_align(b_kind, true)) || !aligned(y, 16))
     return FP8_ERR_ALIGN;
   DeviceInfo* dev = nullptr;
   if (int s = current_device(&dev)) return s;
@@ -140,7 +140,7 @@ int fp8_grouped_gemm(const uint8_t* a_q, const void* a_scale, int a_kind, const 
   if (total_m == 0 || n == 0) return FP8_OK;
   if (!a_q || !a_scale || !b_q || !b_scale || !group_offsets || !y) return FP8_ERR_INVALID_ARG;
   if (!aligned(a_q, 16) || !aligned(b_q, 16) || !aligned(a_scale, 4) || !aligned(b_scale, 4) ||
-      !aligned(group_offsets, 4) || !aligned(y, y_type == FP8_OUT_F32 ? 4 : 2))
+      !aligned(group_offsets, 4) || !aligned(y, 16))
     return FP8_ERR_ALIGN;
   DeviceInfo* dev = nullptr;
   if (int s = current_device(&dev)) return s;

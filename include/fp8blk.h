@@ -138,7 +138,8 @@ int fp8_fake_quant_merge(const uint16_t* w, const uint16_t* lora_b, const uint16
  * multiplication on block-quantized operands).
  *
  * a_q [m x k] codes with a_scale; b_q [n x k] codes with b_scale (both
- * K-contiguous, as produced by fp8_block_quantize; 16-byte aligned).
+ * K-contiguous, as produced by fp8_block_quantize; 16-byte aligned;
+ * E8M0 scale arrays 4-byte aligned, fp32 scale arrays 4-byte aligned).
  * Supported (a_kind, b_kind):
  *   (FP8_BLOCK_1x128_F32, FP8_BLOCK_128x128_F32): per 128-wide K chunk the
  *        FP8 partial product is formed on the matrix cores and added to the
@@ -146,7 +147,8 @@ int fp8_fake_quant_merge(const uint16_t* w, const uint16_t* lora_b, const uint16
  *   (FP8_BLOCK_1x32_E8M0, FP8_BLOCK_1x32_E8M0): MXFP8 x MXFP8, the
  *        power-of-two scales are applied inside the scaled matrix
  *        instruction and accumulation is continuous in fp32.
- * y      [m x n] out, bf16 (RN_bf16 of the fp32 result) or float, per y_type.
+ * y      [m x n] out, bf16 (RN_bf16 of the fp32 result) or float, per y_type
+ *        (16-byte aligned).
  * Shape: m >= 0 (any), n % 128 == 0, k % 128 == 0.
  */
 int fp8_block_scaled_gemm(const uint8_t* a_q, const void* a_scale, int a_kind,
@@ -169,7 +171,7 @@ int fp8_block_scaled_gemm(const uint8_t* a_q, const void* a_scale, int a_kind,
  *     [groups][n/128][k/128]);
  * group_offsets: DEVICE int32 [groups+1], off[0] = 0, non-decreasing,
  *     off[groups] = total_m (not checked: a violation is undefined);
- * y [total_m x n] out, bf16 or float per y_type.
+ * y [total_m x n] out, bf16 or float per y_type (16-byte aligned).
  * Shape: groups >= 1, total_m >= 0, n % 128 == 0, k % 128 == 0.
  */
 int fp8_grouped_gemm(const uint8_t* a_q, const void* a_scale, int a_kind,

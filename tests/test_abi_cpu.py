@@ -87,7 +87,8 @@ def test_gemm_validation(lib):
     assert g(A16, A16, 1, A16, A16, 2, 8, 128, 0, A16, 0, None) == SHAPE         # empty reduction
     assert g(A16 + 1, A16, 1, A16, A16, 2, 8, 128, 128, A16, 0, None) == ALIGN
     assert g(A16, A16, 0, A16, A16 + 1, 0, 8, 128, 128, A16, 0, None) == ALIGN    # E8M0 scales: 4 B
-    assert g(A16, A16, 1, A16, A16, 2, 8, 128, 128, A16 + 2, 1, None) == ALIGN    # f32 out: 4 B
+    assert g(A16, A16, 1, A16, A16, 2, 8, 128, 128, A16 + 4, 1, None) == ALIGN    # y: 16 B
+    assert g(A16, A16, 1, A16, A16, 2, 8, 128, 128, A16 + 2, 0, None) == ALIGN
 
 
 def test_grouped_validation(lib):
