@@ -1,26 +1,33 @@
 """Benchmark of the block-scaled FP8 hot path on one MI355X.
 
-One step = one pass of the path over one batch of synthetic input of the
-DeepSeek-V3-shaped dense projection (weights bf16 2048x7168 quantized in
-128x128 blocks, activations bf16 4096x7168 quantized per token in 1x128
-tiles, block-scaled FP8 GEMM M=4096 N=2048 K=7168, bf16 out):
+One step = one pass of the path over one batch of synthetic input.  The
+default workload is the DeepSeek-V3-shaped dense projection (weights bf16
+2048x7168 quantized in 128x128 blocks, activations bf16 4096x7168 quantized
+per token in 1x128 tiles, block-scaled FP8 GEMM M=4096 N=2048 K=7168 with
+per-128-K promotion, bf16 out):
     fp8_block_quantize(W, 128x128) -> fp8_block_quantize(X, 1x128)
-    -> fp8_block_scaled_gemm(A=X codes, B=W codes)
+    -> fp8_block_scaled_gemm(A = X codes, B = W codes)
 Inputs are resident in HBM before timing starts; several input sets rotate
 so that no step finds its inputs in the 256 MB Infinity Cache.
 
-Prints one JSON line.  ``value`` is the whole step's throughput in GEMM
-TFLOP/s (2*M*N*K per step over the step time); per-kernel times, GB/s and
-roofline fractions are in ``components``; ``roofline`` is the dominant
-kernel (the GEMM) timed with HIP events on the stream it runs on.
+Prints one JSON line.  ``value`` is the step's throughput in GEMM TFLOP/s
+(2*M*N*K per step over the measured step time).  ``roofline`` describes the
+dominant kernel (the GEMM): its average duration comes from HIP events
+recorded around each of its launches inside the timed region, on the stream
+the kernel runs on.  ``components`` gives every kernel's own time, GB/s and
+roofline fraction from a separate, untimed pass with events around each
+launch.
 
 Other workloads (``--config``) print the same kind of line for their own
-path: mx (the MXFP8 small case), qat (merge + fake-quant + GEMM), prequant
-(MXFP8 quantization of one MoE layer's 256 routed experts), moe (per-token
-quantize + grouped expert GEMM).
+path: mx (MXFP8 quantize of W 256x512 and X 64x512, MX x MX GEMM), qat
+(LoRA merge + 128x128 fake-quant of W 7168x7168, 1x128 fake-quant of X
+8192x7168, GEMM 8192x7168x7168), prequant (MXFP8 quantization of one MoE
+layer's 256 routed experts) and moe (per-token quantize of 16384x7168 and
+the grouped gate||up expert GEMM over Zipf(1.1) top-8 routing).
 """
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -32,6 +39,8 @@ import torch
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 FP8_PEAK_TFLOPS = 5000.0     # MI355X dense FP8 MFMA, TFLOP/s
 MALL_BYTES = 256 << 20
+HERE = os.path.dirname(os.path.abspath(__file__))
+METRIC = "FP8 block-scaled GEMM TFLOPS + quantize GB/s, % of MI355X roofline"
 
 
 def _lib():
@@ -40,13 +49,20 @@ def _lib():
     return fb
 
 
-class KernelTimer:
-    """HIP events on the current stream around every launch of each kernel."""
+def _sets_for(bytes_per_set):
+    """Number of rotating input sets so that a step never reads inputs that
+    the previous two steps left in the Infinity Cache."""
+    return max(2, int(np.ceil(2 * MALL_BYTES / bytes_per_set)) + 1)
+
+
+class Events:
+    """HIP event pairs on the current stream (the stream the library's
+    launches go to), grouped by kernel name."""
 
     def __init__(self):
         self.ev = {}
 
-    def __call__(self, name, fn):
+    def around(self, name, fn):
         s = torch.cuda.Event(enable_timing=True)
         e = torch.cuda.Event(enable_timing=True)
         s.record()
@@ -58,13 +74,28 @@ class KernelTimer:
         return {k: float(np.mean([s.elapsed_time(e) for s, e in v])) for k, v in self.ev.items()}
 
 
+class Workload:
+    """A step is a list of (name, launch) pairs; ``bytes``/``flops`` hold
+    each kernel's algorithmic work per launch."""
+
+    def __init__(self, launches, dominant, bound, step_flops, step_bytes, kbytes, kflops, cfg, unit):
+        self.launches = launches          # i -> [(name, fn)]
+        self.dominant = dominant
+        self.bound = bound                # "mfma" or "hbm"
+        self.step_flops = step_flops
+        self.step_bytes = step_bytes
+        self.kbytes = kbytes
+        self.kflops = kflops
+        self.cfg = cfg
+        self.unit = unit                  # unit of ``value``
+
+
 # ----------------------------------------------------------------- workloads
 
 def dense_workload(fb, dev):
     import workloads
     M, N, K = 4096, 2048, 7168
-    per_set = (M * K + N * K) * 2
-    nsets = max(2, int(np.ceil(2 * MALL_BYTES / per_set)) + 1)
+    nsets = _sets_for((M * K + N * K) * 2)
     sets = []
     for i in range(nsets):
         d = workloads.dense_projection(dev, seeds=(200 + 2 * i, 201 + 2 * i))
@@ -75,24 +106,195 @@ def dense_workload(fb, dev):
     xs = torch.empty((M, K // 128), dtype=torch.float32, device=dev)
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
 
-    def step(i, timer):
+    def launches(i):
         w, x = sets[i % nsets]
-        timer("quantize_w_128x128", lambda: fb.fp8_block_quantize(w, "128x128", "ceil", wq, ws))
-        timer("quantize_x_1x128", lambda: fb.fp8_block_quantize(x, "1x128", "ceil", xq, xs))
-        timer("gemm", lambda: fb.fp8_block_scaled_gemm(xq, xs, "1x128", wq, ws, "128x128", y))
+        return [("quantize_w_128x128", lambda: fb.fp8_block_quantize(w, "128x128", "ceil", wq, ws)),
+                ("quantize_x_1x128", lambda: fb.fp8_block_quantize(x, "1x128", "ceil", xq, xs)),
+                ("gemm", lambda: fb.fp8_block_scaled_gemm(xq, xs, "1x128", wq, ws, "128x128", y))]
 
     flops = 2.0 * M * N * K
-    comp_bytes = {
+    kbytes = {
         # algorithmic bytes: read bf16, write codes + scales
         "quantize_w_128x128": N * K * 2 + N * K + (N // 128) * (K // 128) * 4,
         "quantize_x_1x128": M * K * 2 + M * K + M * (K // 128) * 4,
         # GEMM operand/result bytes (reported, not the bound)
         "gemm": M * K + N * K + M * (K // 128) * 4 + (N // 128) * (K // 128) * 4 + M * N * 2,
     }
-    comp_flops = {"gemm": flops}
-    cfg = {"workload": "dense projection W 2048x7168 (128x128) + X 4096x7168 (1x128) + GEMM M4096 N2048 K7168",
+    cfg = {"workload": "dense projection: quantize W 2048x7168 (128x128, fp32 scales) and X 4096x7168 "
+                       "(1x128, fp32 scales), block-scaled FP8 GEMM M4096 N2048 K7168, bf16 out",
            "m": M, "n": N, "k": K, "input_sets": nsets}
-    return step, flops, comp_bytes, comp_flops, cfg, "gemm", sets[0]
+    return Workload(launches, "gemm", "mfma", flops, sum(kbytes.values()), kbytes, {"gemm": flops}, cfg, "TFLOP/s")
+
+
+def mx_workload(fb, dev):
+    import workloads
+    d = workloads.mx_small(dev)
+    w, x = d["w"], d["x"]
+    wq = torch.empty((256, 512), dtype=torch.uint8, device=dev)
+    ws = torch.empty((256, 16), dtype=torch.uint8, device=dev)
+    xq = torch.empty((64, 512), dtype=torch.uint8, device=dev)
+    xs = torch.empty((64, 16), dtype=torch.uint8, device=dev)
+    y = torch.empty((64, 256), dtype=torch.bfloat16, device=dev)
+
+    def launches(i):
+        return [("quantize_w_1x32", lambda: fb.fp8_block_quantize(w, "1x32", "ceil", wq, ws)),
+                ("quantize_x_1x32", lambda: fb.fp8_block_quantize(x, "1x32", "ceil", xq, xs)),
+                ("gemm_mx", lambda: fb.fp8_block_scaled_gemm(xq, xs, "1x32", wq, ws, "1x32", y))]
+
+    flops = 2.0 * 64 * 256 * 512
+    kbytes = {"quantize_w_1x32": 256 * 512 * 3 + 256 * 16, "quantize_x_1x32": 64 * 512 * 3 + 64 * 16,
+              "gemm_mx": 64 * 512 + 256 * 512 + 64 * 16 + 256 * 16 + 64 * 256 * 2}
+    cfg = {"workload": "MXFP8 small case: quantize W 256x512 and X 64x512 (1x32, E8M0), GEMM 64x256x512, "
+                       "bf16 out (launch-latency bound, not roofline-meaningful)", "m": 64, "n": 256, "k": 512}
+    return Workload(launches, "gemm_mx", "mfma", flops, sum(kbytes.values()), kbytes, {"gemm_mx": flops}, cfg,
+                    "TFLOP/s")
+
+
+def qat_workload(fb, dev):
+    import workloads
+    M, N, K, R = 8192, 7168, 7168, 16
+    d = workloads.qat_forward(dev)
+    w, la, lb, x = d["w"], d["lora_a"], d["lora_b"], d["x"]
+    wq = torch.empty((N, K), dtype=torch.uint8, device=dev)
+    ws = torch.empty((N // 128, K // 128), dtype=torch.float32, device=dev)
+    wdq = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+    xq = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    xs = torch.empty((M, K // 128), dtype=torch.float32, device=dev)
+    xdq = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+
+    def launches(i):
+        return [("merge_fake_quant_w", lambda: fb.fp8_fake_quant_merge(w, lb, la, wq, ws, wdq)),
+                ("fake_quant_x_1x128", lambda: fb.fp8_block_quantize(x, "1x128", "ceil", xq, xs, xdq)),
+                ("gemm", lambda: fb.fp8_block_scaled_gemm(xq, xs, "1x128", wq, ws, "128x128", y))]
+
+    flops = 2.0 * M * N * K
+    kbytes = {"merge_fake_quant_w": N * K * 2 + (N * R + R * K) * 2 + N * K + (N // 128) * (K // 128) * 4 + N * K * 2,
+              "fake_quant_x_1x128": M * K * 2 + M * K + M * (K // 128) * 4 + M * K * 2,
+              "gemm": M * K + N * K + M * (K // 128) * 4 + (N // 128) * (K // 128) * 4 + M * N * 2}
+    cfg = {"workload": "QAT fake-quant forward: merge W 7168x7168 + B.A (rank 16) and fake-quantize "
+                       "(128x128), fake-quantize X 8192x7168 (1x128), GEMM M8192 N7168 K7168, bf16 out",
+           "m": M, "n": N, "k": K, "rank": R}
+    return Workload(launches, "gemm", "mfma", flops, sum(kbytes.values()), kbytes, {"gemm": flops}, cfg, "TFLOP/s")
+
+
+def prequant_workload(fb, dev):
+    import workloads
+    E, I, H = 256, 2048, 7168
+    fac = workloads.expert_factors()
+    # experts stacked per matrix shape: [gate; up] rows of every expert, then
+    # every expert's down projection, so that one launch covers each shape
+    gu = torch.empty((E * 2 * I, H), dtype=torch.bfloat16, device=dev)
+    dn = torch.empty((E * H, I), dtype=torch.bfloat16, device=dev)
+    for e in range(E):
+        gate, up, down = workloads.expert_weights(e, dev, fac)
+        gu[e * 2 * I:e * 2 * I + I].copy_(gate)
+        gu[e * 2 * I + I:(e + 1) * 2 * I].copy_(up)
+        dn[e * H:(e + 1) * H].copy_(down)
+        del gate, up, down
+    guq = torch.empty(gu.shape, dtype=torch.uint8, device=dev)
+    gus = torch.empty((gu.shape[0], H // 32), dtype=torch.uint8, device=dev)
+    dnq = torch.empty(dn.shape, dtype=torch.uint8, device=dev)
+    dns = torch.empty((dn.shape[0], I // 32), dtype=torch.uint8, device=dev)
+
+    def launches(i):
+        return [("quantize_gate_up_1x32", lambda: fb.fp8_block_quantize(gu, "1x32", "ceil", guq, gus)),
+                ("quantize_down_1x32", lambda: fb.fp8_block_quantize(dn, "1x32", "ceil", dnq, dns))]
+
+    n_gu, n_dn = gu.numel(), dn.numel()
+    kbytes = {"quantize_gate_up_1x32": n_gu * 3 + n_gu // 32, "quantize_down_1x32": n_dn * 3 + n_dn // 32}
+    cfg = {"workload": "MXFP8 prequant of one MoE layer: 256 experts x {gate, up 2048x7168; down 7168x2048} bf16 "
+                       "(22.5 GB) -> e4m3fn codes + uint8 E8M0 scales per 1x32 block; experts stacked per shape, "
+                       "one launch per shape",
+           "experts": E, "elements": n_gu + n_dn}
+    return Workload(launches, "quantize_gate_up_1x32", "hbm", 0.0, sum(kbytes.values()), kbytes, {}, cfg, "GB/s")
+
+
+def moe_workload(fb, dev):
+    import workloads
+    T, E, N, K = 16384, 256, 4096, 7168
+    tok, off = workloads.zipf_routing()
+    x = workloads.moe_tokens(dev)
+    xq = torch.empty((T, K), dtype=torch.uint8, device=dev)
+    xs = torch.empty((T, K // 128), dtype=torch.float32, device=dev)
+    fb.fp8_block_quantize(x, "1x128", "ceil", xq, xs)
+    idx = tok.to(dev)
+    aq = xq.index_select(0, idx).contiguous()     # rows grouped by expert (gathered outside the timed region)
+    sa = xs.index_select(0, idx).contiguous()
+    bq = torch.empty((E, N, K), dtype=torch.uint8, device=dev)
+    sb = torch.empty((E, N, K // 32), dtype=torch.uint8, device=dev)
+    fac = workloads.expert_factors()
+    for e in range(E):
+        gate, up, _ = workloads.expert_weights(e, dev, fac)
+        fb.fp8_block_quantize(torch.cat([gate, up], 0), "1x32", "ceil", bq[e], sb[e])
+    offt = off.to(dev)
+    total_m = int(off[-1])
+    y = torch.empty((total_m, N), dtype=torch.bfloat16, device=dev)
+
+    def launches(i):
+        return [("quantize_x_1x128", lambda: fb.fp8_block_quantize(x, "1x128", "ceil", xq, xs)),
+                ("grouped_gemm", lambda: fb.fp8_grouped_gemm(aq, sa, "1x128", bq, sb, "1x32", offt, y))]
+
+    flops = 2.0 * total_m * N * K
+    kbytes = {"quantize_x_1x128": T * K * 3 + T * (K // 128) * 4,
+              "grouped_gemm": total_m * K + total_m * (K // 128) * 4 + E * N * K + E * N * (K // 32) +
+                              total_m * N * 2 + (E + 1) * 4}
+    sizes = (off[1:] - off[:-1]).numpy()
+    cfg = {"workload": "MoE gate||up: quantize X 16384x7168 (1x128), grouped block-scaled FP8 GEMM over 256 "
+                       "experts (Zipf(1.1) top-8, sum M 131072, N 4096, K 7168, MXFP8 weights), bf16 out",
+           "total_m": total_m, "n": N, "k": K, "groups": E,
+           "group_m_max": int(sizes.max()), "group_m_min": int(sizes.min()), "group_m_median": float(np.median(sizes))}
+    return Workload(launches, "grouped_gemm", "mfma", flops, sum(kbytes.values()), kbytes, {"grouped_gemm": flops},
+                    cfg, "TFLOP/s")
+
+
+WORKLOADS = {"dense": dense_workload, "mx": mx_workload, "qat": qat_workload, "prequant": prequant_workload,
+             "moe": moe_workload}
+
+
+# ------------------------------------------------------------ traffic record
+
+def _kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "device.h", "launch.h"):
+        with open(os.path.join(HERE, "block_scaled_fp8_amax_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(config):
+    """HBM bytes per launch of the dominant kernel from the committed
+    rocprofv3 counter summary (FETCH_SIZE + WRITE_SIZE, each scaled by the
+    factor a plain copy of known size gives).  None when there is no
+    summary for this workload or the kernel source changed since."""
+    path = os.path.join(HERE, "profiles", f"traffic_{config}.txt")
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                rec[k.strip()] = v.strip()
+    if rec.get("kernel_source_sha256") != _kernel_source_hash():
+        return None
+    try:
+        return float(rec["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ------------------------------------------------------------- cpu baseline
+
+def _oracle_threads():
+    threads = torch.get_num_threads()
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info] + [1])
+    except Exception:  # noqa: BLE001
+        pass
+    return threads
 
 
 def cpu_baseline_dense(sample_rows=256):
@@ -115,14 +317,7 @@ def cpu_baseline_dense(sample_rows=256):
     t4 = time.perf_counter()
     secs = (t1 - t0) + (t2 - t1) + (t4 - t3)
     flops = 2.0 * sample_rows * 2048 * 7168
-    threads = torch.get_num_threads()
-    try:
-        import threadpoolctl
-        info = threadpoolctl.threadpool_info()
-        threads = max([i.get("num_threads", 1) for i in info] + [1])
-    except Exception:  # noqa: BLE001
-        pass
-    return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+    return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": _oracle_threads(), "kind": "oracle",
             "sample": f"1/16 row slice of the step: quantize W rows 0..127 (128x128), quantize X "
                       f"{sample_rows}x7168 (1x128), GEMM {sample_rows}x2048x7168 fp32-accumulated; "
                       f"{secs:.2f} s on the host"}
@@ -130,13 +325,144 @@ def cpu_baseline_dense(sample_rows=256):
 
 # ---------------------------------------------------------------------- main
 
+_SPIN_PER_MS = None
+
+
+def _spin_ms(ms):
+    """Queue a device spin of about ``ms`` milliseconds on the current stream
+    (torch's sleep kernel, calibrated once with events)."""
+    global _SPIN_PER_MS
+    if _SPIN_PER_MS is None:
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        torch.cuda._sleep(1_000_000)
+        e1.record()
+        torch.cuda.synchronize()
+        _SPIN_PER_MS = 1_000_000 / max(e0.elapsed_time(e1), 1e-3)
+    torch.cuda._sleep(int(min(ms, 2000.0) * _SPIN_PER_MS))
+
+
+def run(args):
+    fb = _lib()
+    dev = "cuda"
+    wl = WORKLOADS[args.config](fb, dev)
+    torch.cuda.synchronize()
+    for i in range(args.warmup):
+        for _, fn in wl.launches(i):
+            fn()
+    torch.cuda.synchronize()
+
+    # host cost of enqueueing one step (the GPU runs behind the host here)
+    h0 = time.perf_counter()
+    for i in range(max(1, args.warmup)):
+        for _, fn in wl.launches(i):
+            fn()
+    host_ms = (time.perf_counter() - h0) * 1e3 / max(1, args.warmup)
+    torch.cuda.synchronize()
+
+    # timed region: K whole steps; events only around the dominant kernel.
+    # A spin kernel queued first keeps the GPU busy while the host enqueues
+    # the steps, so the GPU-side timestamps see back-to-back device work and
+    # not the host's launch overhead.
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    _spin_ms(1.5 * host_ms * args.steps + 2.0)
+    t_start.record()
+    for i in range(args.steps):
+        for name, fn in wl.launches(args.warmup + i):
+            if name == wl.dominant:
+                pairs[i][0].record()
+                fn()
+                pairs[i][1].record()
+            else:
+                fn()
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+    dom_ms = float(np.mean([s.elapsed_time(e) for s, e in pairs]))
+
+    # untimed pass: every kernel on its own
+    comp = Events()
+    torch.cuda.synchronize()
+    nc = max(1, min(args.steps, 10))
+    _spin_ms(1.5 * host_ms * nc + 2.0)
+    for i in range(nc):
+        for name, fn in wl.launches(i):
+            comp.around(name, fn)
+    torch.cuda.synchronize()
+    components = {}
+    for name, ms in comp.mean_ms().items():
+        c = {"us": ms * 1e3}
+        if name in wl.kbytes:
+            c["GB/s"] = wl.kbytes[name] / (ms * 1e-3) / 1e9
+            c["hbm_frac"] = c["GB/s"] / HBM_PEAK_GBS
+        if name in wl.kflops:
+            c["TFLOP/s"] = wl.kflops[name] / (ms * 1e-3) / 1e12
+            c["mfma_frac"] = c["TFLOP/s"] / FP8_PEAK_TFLOPS
+        components[name] = c
+
+    if wl.bound == "mfma":
+        achieved = wl.kflops[wl.dominant] / (dom_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / FP8_PEAK_TFLOPS}
+    else:
+        achieved = wl.kbytes[wl.dominant] / (dom_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS}
+    roof["traffic"] = recorded_traffic(args.config)
+    roof["kernel"] = wl.dominant
+    roof["kernel_us"] = dom_ms * 1e3
+    roof["host_enqueue_us_per_step"] = host_ms * 1e3
+
+    if wl.unit == "TFLOP/s":
+        value = wl.step_flops / (ms_per_step * 1e-3) / 1e12
+    else:
+        value = wl.step_bytes / (ms_per_step * 1e-3) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": wl.unit,
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8",
+        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) activations with 1% channels x50)",
+        "config": wl.cfg,
+        "components": components,
+        "roofline": roof,
+    }
+    if args.config == "dense" and not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_dense()
+    print(json.dumps(out), flush=True)
+
+
+def copy_calibration(args):
+    """Plain device copies of a known size, for scaling the FETCH_SIZE and
+    WRITE_SIZE counters (run under rocprofv3 --pmc)."""
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    for _ in range(max(1, args.steps)):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": max(1, args.steps)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="dense", choices=["dense"])
+    ap.add_argument("--config", default="dense", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run 1 GiB device copies (counter calibration under rocprofv3)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this library has no multi-GPU path "
@@ -145,56 +471,10 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
-    fb = _lib()
-    dev = "cuda"
-    step, flops, comp_bytes, comp_flops, cfg, dominant, _ = dense_workload(fb, dev)
-    torch.cuda.synchronize()
-    warm = KernelTimer()
-    for i in range(args.warmup):
-        step(i, warm)
-    torch.cuda.synchronize()
-    timer = KernelTimer()
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record()
-    for i in range(args.steps):
-        step(args.warmup + i, timer)
-    t_end.record()
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    ms_per_step = total_ms / args.steps
-    kms = timer.mean_ms()
-    components = {}
-    for name, ms in kms.items():
-        c = {"us": ms * 1e3}
-        if name in comp_bytes:
-            c["GB/s"] = comp_bytes[name] / (ms * 1e-3) / 1e9
-            c["hbm_frac"] = c["GB/s"] / HBM_PEAK_GBS
-        if name in comp_flops:
-            c["TFLOP/s"] = comp_flops[name] / (ms * 1e-3) / 1e12
-            c["mfma_frac"] = c["TFLOP/s"] / FP8_PEAK_TFLOPS
-        components[name] = c
-    dom_ms = kms[dominant]
-    achieved = comp_flops[dominant] / (dom_ms * 1e-3) / 1e12
-    roof = {"bound": "mfma", "achieved": achieved, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": achieved / FP8_PEAK_TFLOPS, "traffic": None, "kernel": "gemm_kernel<kF32xF32,bf16>"}
-    out = {
-        "metric": "FP8 block-scaled GEMM TFLOPS + quantize GB/s, % of MI355X roofline",
-        "value": flops / (ms_per_step * 1e-3) / 1e12,
-        "unit": "TFLOP/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "fp8_e4m3fn x fp8_e4m3fn -> fp32 accumulate, bf16 out",
-        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) activations with 1% channels x50)",
-        "config": cfg,
-        "components": components,
-        "roofline": roof,
-    }
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline_dense()
-    print(json.dumps(out), flush=True)
+    if args.copy_calibration:
+        copy_calibration(args)
+    else:
+        run(args)
 
 
 if __name__ == "__main__":

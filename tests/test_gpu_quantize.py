@@ -4,7 +4,8 @@ Codes, scales and fake-quant outputs must equal the oracle's bytes.  Cases:
 shapes spanning several blocks and ragged row counts, every block kind and
 E8M0 rule, an exhaustive-per-mantissa domain sweep of (x, amax) pairs, the
 degenerate blocks (all zero, signed zeros, subnormal and huge amax), the
-full-size activation/weight shapes of the dense and QAT projections, and
+full-size activation/weight shapes of the dense and QAT projections, the
+MXFP8 prequantization of a whole MoE layer's routed experts, and
 determinism across repetitions and launch geometries.
 """
 
@@ -12,9 +13,11 @@ import numpy as np
 import pytest
 import torch
 
+import block_scaled_fp8_amax_amd as fb
+
 from oracle import codec, quant
 from tests.gpu_helpers import assert_bytes_equal, bf16_from_bits, run_quantize
-from workloads import bf16_bits, dense_projection, mx_small, qat_forward
+from workloads import bf16_bits, dense_projection, expert_factors, expert_weights, mx_small, qat_forward
 
 pytestmark = pytest.mark.gpu
 
@@ -161,6 +164,52 @@ def test_qat_activations_full_size_sampled():
     assert_bytes_equal(q[rows], oq, "codes")
     assert_bytes_equal(s[rows], os_, "scales")
     assert_bytes_equal(xdq[rows], oxdq, "dequant")
+
+
+def test_prequant_moe_layer_full_size():
+    """All 256 routed experts of one MoE layer (gate, up 2048x7168 and down
+    7168x2048 each, 22.5 GB of bf16), stacked per matrix shape and quantized
+    to MXFP8 in one launch per shape.  Sampled rows of several experts are
+    compared with the oracle byte for byte; over the whole output, every
+    nonzero block's largest code lies in [224, 448] (the CEIL invariant
+    224 < amax * 2^-X <= 448 survives the rounding to e4m3)."""
+    E, I, H = 256, 2048, 7168
+    fac = expert_factors()
+    gu = torch.empty((E * 2 * I, H), dtype=torch.bfloat16, device="cuda")
+    dn = torch.empty((E * H, I), dtype=torch.bfloat16, device="cuda")
+    for e in range(E):
+        gate, up, down = expert_weights(e, "cuda", fac)
+        gu[e * 2 * I:e * 2 * I + I].copy_(gate)
+        gu[e * 2 * I + I:(e + 1) * 2 * I].copy_(up)
+        dn[e * H:(e + 1) * H].copy_(down)
+        del gate, up, down
+    print("[quantize] MoE layer prequant: gate||up 1048576x7168 and down 1835008x2048, 1x32", flush=True)
+    outs = {}
+    for name, x in (("gate_up", gu), ("down", dn)):
+        rows, cols = x.shape
+        q = torch.empty((rows, cols), dtype=torch.uint8, device="cuda")
+        sc = torch.empty((rows, cols // 32), dtype=torch.uint8, device="cuda")
+        fb.fp8_block_quantize(x, "1x32", "ceil", q, sc)
+        outs[name] = (x, q, sc)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(11)
+    experts = sorted({0, 255} | set(int(v) for v in rng.choice(E, 4, replace=False)))
+    for name, (x, q, sc) in outs.items():
+        per = x.shape[0] // E
+        for e in experts:
+            rows = e * per + np.sort(rng.choice(per, 48, replace=False))
+            idx = torch.from_numpy(rows).cuda()
+            oq, os_, _ = quant.quantize(bf16_bits(x.index_select(0, idx)), "1x32", "ceil")
+            assert_bytes_equal(q.index_select(0, idx).cpu().numpy(), oq, f"{name} codes expert {e}")
+            assert_bytes_equal(sc.index_select(0, idx).cpu().numpy(), os_, f"{name} scales expert {e}")
+        # whole-output invariant, one expert at a time
+        for e in range(E):
+            qe = q[e * per:(e + 1) * per]
+            mag = qe.view(torch.float8_e4m3fn).float().abs().reshape(per, -1, 32).amax(-1)
+            nz = mag > 0
+            assert bool(((mag >= 224) & (mag <= 448))[nz].all()), f"{name} expert {e}"
+            assert int(sc[e * per:(e + 1) * per].max()) <= 254
+    print(f"[quantize] MoE layer prequant checked experts {experts}", flush=True)
 
 
 def test_determinism_and_geometry():
