@@ -130,10 +130,13 @@ def _grouped(aq, sa, bq, sb, bkind, off, out=torch.float32):
     return y
 
 
+@pytest.mark.parametrize("n", [256, 384, 512])
 @pytest.mark.parametrize("bkind", ["1x32", "128x128"])
-def test_grouped_edge_cases(bkind):
+def test_grouped_edge_cases(bkind, n):
+    """Empty groups (first, middle, last), 1 row, tile-boundary sizes, and n
+    both a multiple of 256 (128x256 tiles) and not (256x128 tiles)."""
     sizes = [0, 1, 127, 128, 129, 0, 300, 5, 0]
-    g, n, k = len(sizes), 256, 512
+    g, k = len(sizes), 512
     off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
     total = int(off[-1])
     aq, sa = _q(_rand_bf16((total, k), 1.0, 10), "1x128")
@@ -150,6 +153,32 @@ def test_grouped_edge_cases(bkind):
         lo, hi = off[e], off[e + 1]
         assert gemm.normwise_rel_err(y32[lo:hi], ref[e]) <= TOL, e
     assert np.array_equal(y16, codec.f32_to_bf16(y32))
+
+
+@pytest.mark.parametrize("bkind", ["1x32", "128x128"])
+def test_grouped_many_groups(bkind):
+    """1000 groups of random sizes 0..400 (a quarter of them empty): more
+    groups than threads in the tile-order scan and a tile count that is not
+    a multiple of the XCD count; every group is checked."""
+    rng = np.random.default_rng(31)
+    g, n, k = 1000, 256, 256
+    sizes = rng.integers(0, 401, g)
+    sizes[rng.choice(g, g // 4, replace=False)] = 0
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    total = int(off[-1])
+    aq, sa = _q(_rand_bf16((total, k), 1.0, 40), "1x128")
+    bq, sb = _q(_rand_bf16((g * n, k), 0.02, 41), bkind)
+    bq = bq.view(g, n, k)
+    sb = sb.view(g, n, k // 32) if bkind == "1x32" else sb.view(g, n // 128, k // 128)
+    offt = torch.from_numpy(off).cuda()
+    print(f"[grouped] {g} groups {bkind} total rows {total}", flush=True)
+    y32 = _grouped(aq, sa, bq, sb, bkind, offt).cpu().numpy()
+    ref = gemm.grouped_gemm_ref(aq.cpu().numpy(), sa.cpu().numpy(), "1x128", bq.cpu().numpy(),
+                                sb.cpu().numpy(), bkind, off)
+    for e in range(g):
+        lo, hi = off[e], off[e + 1]
+        if hi > lo:
+            assert gemm.normwise_rel_err(y32[lo:hi], ref[e]) <= TOL, e
 
 
 def test_grouped_moe_full():
