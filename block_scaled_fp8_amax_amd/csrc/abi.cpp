@@ -94,7 +94,7 @@ int fp8_block_quantize(const uint16_t* x, int64_t rows, int64_t cols, int kind, 
 int fp8_fake_quant_merge(const uint16_t* w, const uint16_t* lora_b, const uint16_t* lora_a, int64_t n, int64_t k,
                          int64_t r, uint8_t* q, float* scale, uint16_t* wdq, void* stream) {
   if (r < 1 || r > 64) return FP8_ERR_INVALID_ARG;
-  if (n < 0 || k < 0 || n % 128 || k % 128 || n / 128 > 65535) return FP8_ERR_SHAPE;
+  if (n < 0 || k < 0 || n % 128 || k % 128 || n / 128 > 65535 || k > (int64_t(1) << 24)) return FP8_ERR_SHAPE;
   if (n == 0 || k == 0) return FP8_OK;
   if (!w || !lora_b || !lora_a || !q || !scale) return FP8_ERR_INVALID_ARG;
   if (!aligned(w, 16) || !aligned(q, 16) || !aligned(scale, 4) || !aligned(lora_a, 4) || !aligned(lora_b, 2) ||

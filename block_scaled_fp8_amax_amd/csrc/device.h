@@ -122,6 +122,15 @@ __device__ __forceinline__ float f32_quot(float x, const F32Block& b) {
   return __uint_as_float((__float_as_uint(q) & 0x7FFFFFFFu) | (__float_as_uint(x) & 0x80000000u));
 }
 
+// f32_quot for a block whose prescale is 1 (amax >= 2^-60): the same
+// operations without the multiplications by 1.
+__device__ __forceinline__ float f32_quot_unit(float x, const F32Block& b) {
+  float q0 = x * b.y;
+  float r = __builtin_fmaf(-q0, b.sp, x);
+  float q = __builtin_fmaf(r, b.y, q0);
+  return __uint_as_float((__float_as_uint(q) & 0x7FFFFFFFu) | (__float_as_uint(x) & 0x80000000u));
+}
+
 // ---------------------------------------------------------------- E8M0 scale
 
 // E8M0 code of a block from its bf16 amax bit pattern.

@@ -123,7 +123,7 @@ int fp8_block_quantize(const uint16_t* x, int64_t rows, int64_t cols, int kind, 
  *        (w 16-byte aligned; lora_b, lora_a 4-byte aligned).
  * q      [n x k] codes out; scale float [n/128][k/128] out;
  * wdq    optional [n x k] bf16 fake-quant output (NULL = not written).
- * Shape: n % 128 == 0, k % 128 == 0, 1 <= r <= 64.
+ * Shape: n % 128 == 0, k % 128 == 0, k <= 2^24, 1 <= r <= 64.
  */
 int fp8_fake_quant_merge(const uint16_t* w, const uint16_t* lora_b, const uint16_t* lora_a,
                          int64_t n, int64_t k, int64_t r, uint8_t* q, float* scale,
