@@ -37,6 +37,8 @@
 // last 16 (g = l / 16).  The scale operand of lane L applies to row L % 16
 // and the 32-wide K block L / 16.  The 16x16 fp32 result gives lane l
 // column l % 16 and rows 4*(l/16) + v, v = 0..3.
+#include <type_traits>
+
 #include "device.h"
 #include "launch.h"
 
@@ -300,14 +302,21 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmParams p) {
     s_off = 0;
     s_lds = L::kA + L::kB + L::kSA + j * 256;
   }
-  auto issue = [&](int kb) {
+  constexpr int PER = A_PER + B_PER + 1;
+  // load i (0 .. PER-1) of this wave's share of stage kb
+  auto issue_one = [&](int kb, int i) {
     const uint32_t sbase = lds0 + (kb % STAGES) * L::kStage;
     const uint32_t koff = (uint32_t)kb * kBK;
+    if (i < A_PER)
+      dma16(aq, a_off[i] + koff, sbase + (i * NW + wave) * 1024);
+    else if (i < A_PER + B_PER)
+      dma16(bt, b_off[i - A_PER] + koff, sbase + L::kA + ((i - A_PER) * NW + wave) * 1024);
+    else
+      dma4(s_base, s_off + (uint32_t)kb * 4, sbase + s_lds);
+  };
+  auto issue = [&](int kb) {
 #pragma unroll
-    for (int j = 0; j < A_PER; ++j) dma16(aq, a_off[j] + koff, sbase + (j * NW + wave) * 1024);
-#pragma unroll
-    for (int j = 0; j < B_PER; ++j) dma16(bt, b_off[j] + koff, sbase + L::kA + (j * NW + wave) * 1024);
-    dma4(s_base, s_off + (uint32_t)kb * 4, sbase + s_lds);
+    for (int i = 0; i < PER; ++i) issue_one(kb, i);
   };
 
   v4f acc[4][4];
@@ -323,8 +332,11 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmParams p) {
   float sbk = 1.f;
   int xa[4], xb[4];
 
-  // memory phase: fragments and scales of step kb into registers
-  auto mem_phase = [&](int kb) {
+  // memory phase: fragments and scales of step kb into registers, with this
+  // wave's loads of stage kb+2 interleaved between the fragment reads (a
+  // load waiting on the address unit then does not hold back LDS reads)
+  auto mem_phase = [&](int kb, auto do_load_t) {
+    constexpr bool do_load = decltype(do_load_t)::value;
     const uint8_t* sA = smem + (kb % STAGES) * L::kStage;
     const uint8_t* sB = sA + L::kA;
     const uint32_t* sSA = reinterpret_cast<const uint32_t*>(sA + L::kA + L::kB);
@@ -335,6 +347,7 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmParams p) {
       const uint8_t* rowp = sA + ar * kBK;
       const int s0 = (fg ^ swz(ar)) * 16;
       af[mi] = make_frag(*reinterpret_cast<const u32x4*>(rowp + s0), *reinterpret_cast<const u32x4*>(rowp + (s0 ^ 64)));
+      if constexpr (do_load) issue_one(kb + STAGES - 1, mi);
       if constexpr (A_MX) {
         xa[mi] = (int)((sSA[ar] >> (8 * fg)) & 0xFFu);
       } else {
@@ -351,10 +364,16 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmParams p) {
       const uint8_t* rowp = sB + bc * kBK;
       const int s0 = (fg ^ swz(bc)) * 16;
       bfr[ni] = make_frag(*reinterpret_cast<const u32x4*>(rowp + s0), *reinterpret_cast<const u32x4*>(rowp + (s0 ^ 64)));
+      if constexpr (do_load) {
+        if (4 + ni < PER) issue_one(kb + STAGES - 1, 4 + ni);
+      }
       if constexpr (B_MX) xb[ni] = (int)((sSB[bc] >> (8 * fg)) & 0xFFu);
     }
     if constexpr (MODE == kF32xF32) sbk = __uint_as_float(sSB[(wn >> 1) * 64]);
-    if (kb + STAGES - 1 < KB) issue(kb + STAGES - 1);
+    if constexpr (do_load) {
+#pragma unroll
+      for (int i = 8; i < PER; ++i) issue_one(kb + STAGES - 1, i);
+    }
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the stage may be refilled after the next barrier
   };
 
@@ -428,26 +447,32 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmParams p) {
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("" ::: "memory");
   };
-  constexpr int PER = A_PER + B_PER + 1;
+  // The loops are split where the loads of later stages run out, so that
+  // the loop bodies carry no branch around the loads.
+  const int kl = KB > STAGES - 1 ? KB - (STAGES - 1) : 0;
   if (grp == 0) {
-    for (int kb = 0; kb < KB; ++kb) {
+    auto step = [&](int kb, auto do_load) {
       wait_stage(kb, PER);
       half_barrier();              // half-step 2kb: memory
-      mem_phase(kb);
+      mem_phase(kb, do_load);
       half_barrier();              // half-step 2kb+1: compute
       compute_phase();
-    }
+    };
+    for (int kb = 0; kb < kl; ++kb) step(kb, std::true_type{});
+    for (int kb = kl; kb < KB; ++kb) step(kb, std::false_type{});
     half_barrier();                // half-step 2KB
   } else {
     wait_stage(0, PER);
     half_barrier();                // half-step 0
-    for (int kb = 0; kb < KB; ++kb) {
+    auto step = [&](int kb, auto do_load) {
       half_barrier();              // half-step 2kb+1: memory
-      mem_phase(kb);
+      mem_phase(kb, do_load);
       if (kb + 1 < KB) wait_stage(kb + 1, PER);
       half_barrier();              // half-step 2kb+2: compute
       compute_phase();
-    }
+    };
+    for (int kb = 0; kb < kl; ++kb) step(kb, std::true_type{});
+    for (int kb = kl; kb < KB; ++kb) step(kb, std::false_type{});
   }
 
   // ---- epilogue: stage the tile in LDS, then write whole rows with 16-byte
