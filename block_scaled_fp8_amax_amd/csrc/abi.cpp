@@ -136,7 +136,7 @@ int fp8_grouped_gemm(const uint8_t* a_q, const void* a_scale, int a_kind, const 
     return FP8_ERR_UNSUPPORTED;
   if (groups < 1 || groups > 1024) return FP8_ERR_INVALID_ARG;
   if (total_m < 0 || n < 0 || k <= 0 || n % 128 || k % 128) return FP8_ERR_SHAPE;
-  if (total_m > 0x7FFFFFFF || (total_m / 128 + groups) * (n / 128) > 0x7FFFFFFF) return FP8_ERR_SHAPE;
+  if (total_m > 0x7FFFFFFF || (total_m / 128 + groups) * (n / 128) > 0x7FFFFF00) return FP8_ERR_SHAPE;
   if (total_m == 0 || n == 0) return FP8_OK;
   if (!a_q || !a_scale || !b_q || !b_scale || !group_offsets || !y) return FP8_ERR_INVALID_ARG;
   if (!aligned(a_q, 16) || !aligned(b_q, 16) || !aligned(a_scale, 4) || !aligned(b_scale, 4) ||

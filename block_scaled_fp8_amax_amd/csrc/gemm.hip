@@ -126,11 +126,12 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
 // Grouped tile order.  Every workgroup rebuilds, in LDS, the number of
 // m-tiles of each group (ceil(M_g / BM)) and their prefix sums; the tiles
 // of group g are numbered after those of groups 0..g-1, banded inside the
-// group like the dense order.  The grid is an upper bound (total_m/BM +
-// groups m-tile slots per n-tile); of the T real tiles, XCD x (workgroups
-// i = x mod 8) takes a contiguous range of T/8 (one more for the first
-// T mod 8 XCDs), so that the tiles an XCD runs at once share A rows and
-// B columns in its L2.  Workgroups i >= T return at once.
+// group like the dense order.  Consecutive runs of 32 tiles ("windows",
+// one per CU of an XCD) share A rows and B columns; window w runs on XCD
+// w mod 8, so each XCD sees a mix of large (compute-bound) and small
+// (memory-bound) groups.  The grid is an upper bound (total_m/BM + groups
+// m-tile slots per n-tile, rounded up to a multiple of 256); workgroups
+// whose tile index reaches the real count T return at once.
 // `scratch` is LDS of at least 2 * 1025 ints; returns false when workgroup
 // blockIdx.x has no tile.
 template <int BM>
@@ -157,9 +158,9 @@ __device__ __forceinline__ bool grouped_tile(const GemmParams& p, int* scratch, 
   const int tiles_n = p.tiles_n;
   const int T = s_pref[groups] * tiles_n;
   const int i = (int)blockIdx.x;
-  if (i >= T) return false;
-  const int x = i & 7, q = T >> 3, rem = T & 7;
-  const int L = x * q + (x < rem ? x : rem) + (i >> 3);
+  const int j = i >> 3;                                    // index among this XCD's workgroups
+  const int L = ((((j >> 5) << 3) + (i & 7)) << 5) + (j & 31);
+  if (L >= T) return false;
   const int slot = L / tiles_n;
   int lo = 0, hi = groups - 1;  // g with s_pref[g] <= slot < s_pref[g+1]
   while (lo < hi) {
@@ -571,8 +572,9 @@ hipError_t launch_grouped_gemm(const uint8_t* a, const void* sa, int a_kind, con
   const int bm = wide ? 128 : 256;
   p.tiles_n = (int)(wide ? n / 256 : n / 128);
   const int64_t slots = total_m / bm + groups;   // >= sum over groups of ceil(M_g / bm)
-  if (slots * p.tiles_n > 0x7FFFFFFF) return hipErrorInvalidValue;
-  dim3 grid((unsigned)(slots * p.tiles_n));
+  const int64_t wgs = (slots * p.tiles_n + 255) / 256 * 256;
+  if (wgs > 0x7FFFFFFF) return hipErrorInvalidValue;
+  dim3 grid((unsigned)wgs);
   if (b_kind == 0) {
     if (wide) launch_pp<kF32xMX, true, 128, 256>(p, grid, out_f32, stream);
     else launch_pp<kF32xMX, true, 256, 128>(p, grid, out_f32, stream);
