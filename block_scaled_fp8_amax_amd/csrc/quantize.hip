@@ -13,8 +13,12 @@
 //                 scale array is in block order.  One 16-byte load per lane
 //                 holds 8 bf16; a block is 4 (1x32) or 16 (1x128) adjacent
 //                 lanes, reduced with DPP lane permutations.  Each wave
-//                 streams U chunks per lane per iteration (4 KiB of bf16 in
-//                 flight per wave) over a grid-stride loop.
+//                 handles U chunks per lane (4 KiB of bf16 in flight per
+//                 wave), one pass per workgroup: the grid covers the whole
+//                 matrix, so retiring workgroups are replaced by new ones
+//                 whose loads are issued at once (measured faster than a
+//                 capped grid walking the matrix in a grid-stride loop,
+//                 which serializes each wave's loads behind its stores).
 //   quant_128   : 128x128 blocks, one 256-thread workgroup per block; every
 //                 thread keeps its 64 elements in registers between the amax
 //                 pass and the encode pass, so the block is read once.
@@ -158,7 +162,8 @@ __global__ __launch_bounds__(256) void quant_128_kernel(const uint16_t* __restri
 static int rows_grid(int64_t nchunks, int num_cu) {
   const int64_t per_block = (int64_t)(kQRowsThreads / 64) * 64 * kQRowsU;  // chunks per workgroup pass
   int64_t need = (nchunks + per_block - 1) / per_block;
-  const int64_t cap = (int64_t)num_cu * 8;
+  (void)num_cu;
+  const int64_t cap = int64_t(1) << 30;   // the loop below covers any remainder
   if (need > cap) need = cap;
   if (need < 1) need = 1;
   return (int)need;
