@@ -22,8 +22,9 @@ Other workloads (``--config``) print the same kind of line for their own
 path: mx (MXFP8 quantize of W 256x512 and X 64x512, MX x MX GEMM), qat
 (LoRA merge + 128x128 fake-quant of W 7168x7168, 1x128 fake-quant of X
 8192x7168, GEMM 8192x7168x7168), prequant (MXFP8 quantization of one MoE
-layer's 256 routed experts) and moe (per-token quantize of 16384x7168 and
-the grouped gate||up expert GEMM over Zipf(1.1) top-8 routing).
+layer's 256 routed experts), moe (per-token quantize of 16384x7168 and
+the grouped gate||up expert GEMM over Zipf(1.1) top-8 routing) and dequant
+(the MXFP8 MoE layer back to bf16).
 """
 
 import argparse
@@ -210,6 +211,37 @@ def prequant_workload(fb, dev):
     return Workload(launches, "quantize_gate_up_1x32", "hbm", 0.0, sum(kbytes.values()), kbytes, {}, cfg, "GB/s")
 
 
+def dequant_workload(fb, dev):
+    """MXFP8 MoE layer back to bf16: the codes and E8M0 scales of the
+    prequant workload (quantized while setting up) are dequantized."""
+    import workloads
+    E, I, H = 256, 2048, 7168
+    fac = workloads.expert_factors()
+    guq = torch.empty((E * 2 * I, H), dtype=torch.uint8, device=dev)
+    gus = torch.empty((E * 2 * I, H // 32), dtype=torch.uint8, device=dev)
+    dnq = torch.empty((E * H, I), dtype=torch.uint8, device=dev)
+    dns = torch.empty((E * H, I // 32), dtype=torch.uint8, device=dev)
+    for e in range(E):
+        gate, up, down = workloads.expert_weights(e, dev, fac)
+        fb.fp8_block_quantize(torch.cat([gate, up], 0), "1x32", "ceil", guq[e * 2 * I:(e + 1) * 2 * I],
+                              gus[e * 2 * I:(e + 1) * 2 * I])
+        fb.fp8_block_quantize(down, "1x32", "ceil", dnq[e * H:(e + 1) * H], dns[e * H:(e + 1) * H])
+        del gate, up, down
+    gux = torch.empty(guq.shape, dtype=torch.bfloat16, device=dev)
+    dnx = torch.empty(dnq.shape, dtype=torch.bfloat16, device=dev)
+
+    def launches(i):
+        return [("dequantize_gate_up_1x32", lambda: fb.fp8_block_dequantize(guq, gus, "1x32", gux)),
+                ("dequantize_down_1x32", lambda: fb.fp8_block_dequantize(dnq, dns, "1x32", dnx))]
+
+    n_gu, n_dn = guq.numel(), dnq.numel()
+    kbytes = {"dequantize_gate_up_1x32": n_gu * 3 + n_gu // 32, "dequantize_down_1x32": n_dn * 3 + n_dn // 32}
+    cfg = {"workload": "MXFP8 MoE layer to bf16: 256 experts x {gate, up 2048x7168; down 7168x2048} e4m3fn codes "
+                       "+ uint8 E8M0 scales per 1x32 block -> bf16 (22.5 GB written), one launch per shape",
+           "experts": E, "elements": n_gu + n_dn}
+    return Workload(launches, "dequantize_gate_up_1x32", "hbm", 0.0, sum(kbytes.values()), kbytes, {}, cfg, "GB/s")
+
+
 def moe_workload(fb, dev):
     import workloads
     T, E, N, K = 16384, 256, 4096, 7168
@@ -249,7 +281,7 @@ def moe_workload(fb, dev):
 
 
 WORKLOADS = {"dense": dense_workload, "mx": mx_workload, "qat": qat_workload, "prequant": prequant_workload,
-             "moe": moe_workload}
+             "moe": moe_workload, "dequant": dequant_workload}
 
 
 # ------------------------------------------------------------ traffic record

@@ -11,6 +11,7 @@ Block kinds, E8M0 rules and output types mirror the C enums.
 
 import ctypes
 import os
+import re
 
 import torch
 
@@ -18,16 +19,18 @@ __all__ = [
     "FP8_BLOCK_1x32_E8M0", "FP8_BLOCK_1x128_F32", "FP8_BLOCK_128x128_F32",
     "FP8_E8M0_CEIL", "FP8_E8M0_FLOOR", "FP8_OUT_BF16", "FP8_OUT_F32",
     "Fp8Error", "library", "library_path",
-    "fp8_block_quantize", "fp8_fake_quant_merge", "fp8_block_scaled_gemm", "fp8_grouped_gemm",
+    "fp8_block_quantize", "fp8_block_dequantize", "fp8_fake_quant_merge", "fp8_block_scaled_gemm",
+    "fp8_grouped_gemm",
     "fp8_status_string", "fp8_abi_version",
-    "quantize", "fake_quant_merge", "block_scaled_gemm", "grouped_gemm", "scale_shape",
+    "quantize", "dequantize", "fake_quant_merge", "block_scaled_gemm", "grouped_gemm", "scale_shape",
+    "is_routed_expert_weight", "quantize_state_dict",
 ]
 
 FP8_OK = 0
 FP8_BLOCK_1x32_E8M0, FP8_BLOCK_1x128_F32, FP8_BLOCK_128x128_F32 = 0, 1, 2
 FP8_E8M0_CEIL, FP8_E8M0_FLOOR = 0, 1
 FP8_OUT_BF16, FP8_OUT_F32 = 0, 1
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 _KIND_NAMES = {"1x32": FP8_BLOCK_1x32_E8M0, "1x128": FP8_BLOCK_1x128_F32, "128x128": FP8_BLOCK_128x128_F32}
 _RULE_NAMES = {"ceil": FP8_E8M0_CEIL, "floor": FP8_E8M0_FLOOR}
@@ -53,6 +56,8 @@ def library():
         i64, vp, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
         lib.fp8_block_quantize.argtypes = [vp, i64, i64, ci, ci, vp, vp, vp, vp]
         lib.fp8_block_quantize.restype = ci
+        lib.fp8_block_dequantize.argtypes = [vp, vp, i64, i64, ci, vp, vp]
+        lib.fp8_block_dequantize.restype = ci
         lib.fp8_fake_quant_merge.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, vp, vp]
         lib.fp8_fake_quant_merge.restype = ci
         lib.fp8_block_scaled_gemm.argtypes = [vp, vp, ci, vp, vp, ci, i64, i64, i64, vp, ci, vp]
@@ -126,6 +131,15 @@ def fp8_block_quantize(x, kind, rule, q, scale, xdq=None, stream=None):
     st = library().fp8_block_quantize(_ptr(x), rows, cols, _kind(kind), _rule(rule), _ptr(q), _ptr(scale),
                                       _ptr(xdq), _stream(stream, x))
     _check(st, "fp8_block_quantize")
+
+
+def fp8_block_dequantize(q, scale, kind, x, stream=None):
+    """q: uint8/float8_e4m3fn [rows, cols]; scale as written by
+    fp8_block_quantize for ``kind``; x: bf16 [rows, cols] output."""
+    _contig(q, scale, x)
+    rows, cols = q.shape
+    st = library().fp8_block_dequantize(_ptr(q), _ptr(scale), rows, cols, _kind(kind), _ptr(x), _stream(stream, q))
+    _check(st, "fp8_block_dequantize")
 
 
 def fp8_fake_quant_merge(w, lora_b, lora_a, q, scale, wdq=None, stream=None):
@@ -209,3 +223,51 @@ def grouped_gemm(a_q, a_scale, a_kind, b_q, b_scale, b_kind, group_offsets, out_
     y = torch.empty((a_q.shape[0], b_q.shape[1]), dtype=out_dtype, device=a_q.device)
     fp8_grouped_gemm(a_q, a_scale, a_kind, b_q, b_scale, b_kind, group_offsets, y, stream)
     return y
+
+
+def dequantize(q, scale, block, stream=None):
+    """Allocate the bf16 output and run fp8_block_dequantize."""
+    x = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    fp8_block_dequantize(q, scale, block, x, stream)
+    return x
+
+
+# ------------------------------------------- MXFP8 prequantization of experts
+
+# Routed MoE expert projections, prefix-tolerant ("fireworks-prequant 0.1.0",
+# "Formats": model.layers.*.mlp.experts.*.{gate,up,down}_proj.weight); dense,
+# attention, router and shared-expert weights do not match.
+_ROUTED_EXPERT = re.compile(r"(^|\.)layers\.\d+\.mlp\.experts\.\d+\.(gate|up|down)_proj\.weight$")
+
+
+def is_routed_expert_weight(name):
+    return _ROUTED_EXPERT.search(name) is not None
+
+
+def quantize_state_dict(state, fmt="mxfp8", device="cuda", rule="ceil", out_device=None):
+    """Prequantize the routed expert weights of a state dict to MXFP8.
+
+    Every tensor whose name is a routed expert projection weight (bf16,
+    [rows, cols] with cols % 32 == 0) is quantized on ``device`` by
+    fp8_block_quantize with 1x32 blocks and E8M0 scales: ``{..}.weight``
+    becomes the float8_e4m3fn codes and ``{..}.weight_scale_inv`` the uint8
+    E8M0 scale codes [rows, cols/32] ("fireworks-prequant 0.1.0", "Quick
+    start").  Other tensors pass through unchanged (the same objects).
+    Quantized outputs stay on ``device`` unless ``out_device`` is given.
+    """
+    if fmt != "mxfp8":
+        raise ValueError(f"unsupported prequant format {fmt!r} (only 'mxfp8')")
+    out = {}
+    for name, t in state.items():
+        if not is_routed_expert_weight(name):
+            out[name] = t
+            continue
+        if t.dtype != torch.bfloat16 or t.dim() != 2:
+            raise ValueError(f"{name}: expected a 2-D bf16 tensor, got {t.dtype} {tuple(t.shape)}")
+        x = t.to(device).contiguous()
+        q, s = quantize(x, "1x32", rule)
+        if out_device is not None:
+            q, s = q.to(out_device), s.to(out_device)
+        out[name] = q
+        out[name[: -len("weight")] + "weight_scale_inv"] = s
+    return out

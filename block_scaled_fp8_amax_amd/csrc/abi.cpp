@@ -91,6 +91,22 @@ int fp8_block_quantize(const uint16_t* x, int64_t rows, int64_t cols, int kind, 
                                               rule == FP8_E8M0_FLOOR, q, scale, xdq, dev->num_cu, st));
 }
 
+int fp8_block_dequantize(const uint8_t* q, const void* scale, int64_t rows, int64_t cols, int kind, uint16_t* x,
+                         void* stream) {
+  if (!valid_kind(kind)) return FP8_ERR_INVALID_ARG;
+  if (rows < 0 || cols < 0) return FP8_ERR_SHAPE;
+  const int64_t bc = kind == FP8_BLOCK_1x32_E8M0 ? 32 : 128;
+  if (cols % bc) return FP8_ERR_SHAPE;
+  if (kind == FP8_BLOCK_128x128_F32 && rows % 128) return FP8_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return FP8_OK;
+  if (rows * (cols / 8) > 0xFFF00000ll) return FP8_ERR_SHAPE;  // 32-bit chunk indices, with launch margin
+  if (!q || !scale || !x) return FP8_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(x, 16) || !aligned(scale, scale_align(kind, false))) return FP8_ERR_ALIGN;
+  DeviceInfo* dev = nullptr;
+  if (int s = current_device(&dev)) return s;
+  return hip_status(fp8blk::launch_dequant(q, scale, rows, cols, kind, x, reinterpret_cast<hipStream_t>(stream)));
+}
+
 int fp8_fake_quant_merge(const uint16_t* w, const uint16_t* lora_b, const uint16_t* lora_a, int64_t n, int64_t k,
                          int64_t r, uint8_t* q, float* scale, uint16_t* wdq, void* stream) {
   if (r < 1 || r > 64) return FP8_ERR_INVALID_ARG;

@@ -1,0 +1,77 @@
+// Block-scaled FP8 -> bf16 dequantization (gfx950).
+//
+// Method ("FP8 в DeepSeek V3", "Что такое FP8 простыми словами" and "Почему
+// FP8 требует scale factors": FP8 weights are dequantized through the
+// block's inverse scale when an operation needs higher precision;
+// "Практический смысл для инференс-инфраструктуры": FP8 weights can be
+// converted to BF16): x = RN_bf16(RN32(decode(q) * scale)), the same value
+// as the fake-quant output of the quantizer.
+//
+// Layout: the code matrix is a flat array of 8-code chunks (8 bytes); a
+// chunk never crosses a row (cols is a multiple of 32) nor a block, so it
+// has a single scale.  A lane handles U chunks, each one 8-byte load of
+// codes, one scale load, 4 packed fp8 -> fp32 conversions, 8 multiplies and
+// one 16-byte bf16 store, so that every wave-wide store writes 1 KiB of
+// contiguous memory.  One pass per workgroup over a grid that covers the
+// matrix.
+#include "device.h"
+#include "launch.h"
+
+namespace fp8blk {
+
+constexpr int kDqThreads = 256;
+constexpr int kDqU = 4;
+
+// KIND: 0 = 1x32 E8M0, 1 = 1x128 fp32, 2 = 128x128 fp32 (the fp8_block values)
+template <int KIND>
+__global__ __launch_bounds__(kDqThreads) void dequant_kernel(const u32x2* __restrict__ q, uint32_t nchunks,
+                                                             uint32_t cpr, int64_t cols, const void* __restrict__ scale,
+                                                             u32x4* __restrict__ x) {
+  const uint32_t first = blockIdx.x * (uint32_t)(kDqThreads * kDqU) + threadIdx.x;
+  u32x2 c[kDqU];
+#pragma unroll
+  for (int u = 0; u < kDqU; ++u) {
+    const uint32_t idx = first + u * kDqThreads;
+    c[u] = idx < nchunks ? __builtin_nontemporal_load(q + idx) : (u32x2){0u, 0u};
+  }
+#pragma unroll
+  for (int u = 0; u < kDqU; ++u) {
+    const uint32_t idx = first + u * kDqThreads;
+    if (idx >= nchunks) continue;
+    const uint32_t row = idx / cpr;                     // cpr = cols / 8 chunks per row
+    const int64_t col = (int64_t)(idx - row * cpr) * 8;
+    float s;
+    if constexpr (KIND == 0) {
+      s = e8m0_val(reinterpret_cast<const uint8_t*>(scale)[(int64_t)row * (cols / 32) + col / 32]);
+    } else if constexpr (KIND == 1) {
+      s = reinterpret_cast<const float*>(scale)[(int64_t)row * (cols / 128) + col / 128];
+    } else {
+      s = reinterpret_cast<const float*>(scale)[(int64_t)(row / 128) * (cols / 128) + col / 128];
+    }
+    float d[8];
+    decode4_e4m3(c[u].x, d);
+    decode4_e4m3(c[u].y, d + 4);
+    const u32x4 o = {pack_bf16x2(d[0] * s, d[1] * s), pack_bf16x2(d[2] * s, d[3] * s),
+                     pack_bf16x2(d[4] * s, d[5] * s), pack_bf16x2(d[6] * s, d[7] * s)};
+    __builtin_nontemporal_store(o, x + idx);
+  }
+}
+
+hipError_t launch_dequant(const uint8_t* q, const void* scale, int64_t rows, int64_t cols, int kind, uint16_t* x,
+                          hipStream_t stream) {
+  const uint32_t nchunks = (uint32_t)(rows * cols / 8);
+  const uint32_t cpr = (uint32_t)(cols / 8);
+  const uint32_t per_wg = kDqThreads * kDqU;
+  const dim3 grid((nchunks + per_wg - 1) / per_wg);
+  const u32x2* qv = reinterpret_cast<const u32x2*>(q);
+  u32x4* xv = reinterpret_cast<u32x4*>(x);
+  if (kind == 0)
+    hipLaunchKernelGGL((dequant_kernel<0>), grid, dim3(kDqThreads), 0, stream, qv, nchunks, cpr, cols, scale, xv);
+  else if (kind == 1)
+    hipLaunchKernelGGL((dequant_kernel<1>), grid, dim3(kDqThreads), 0, stream, qv, nchunks, cpr, cols, scale, xv);
+  else
+    hipLaunchKernelGGL((dequant_kernel<2>), grid, dim3(kDqThreads), 0, stream, qv, nchunks, cpr, cols, scale, xv);
+  return hipGetLastError();
+}
+
+}  // namespace fp8blk

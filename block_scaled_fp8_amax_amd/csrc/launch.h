@@ -11,6 +11,8 @@ hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, int 
                              void* scale, uint16_t* xdq, int num_cu, hipStream_t stream);
 hipError_t launch_quant_128(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* q, float* scale, uint16_t* xdq,
                             hipStream_t stream);
+hipError_t launch_dequant(const uint8_t* q, const void* scale, int64_t rows, int64_t cols, int kind, uint16_t* x,
+                          hipStream_t stream);
 hipError_t launch_merge(const uint16_t* w, const uint16_t* lb, const uint16_t* la, int64_t n, int64_t k, int64_t r,
                         uint8_t* q, float* scale, uint16_t* wdq, hipStream_t stream);
 hipError_t launch_gemm(const uint8_t* a, const void* sa, int a_kind, const uint8_t* b, const void* sb, int b_kind,

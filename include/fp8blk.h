@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define FP8BLK_ABI_VERSION 1
+#define FP8BLK_ABI_VERSION 2
 
 typedef enum {
   FP8_OK = 0,
@@ -104,6 +104,30 @@ typedef enum { FP8_OUT_BF16 = 0, FP8_OUT_F32 = 1 } fp8_out;
  */
 int fp8_block_quantize(const uint16_t* x, int64_t rows, int64_t cols, int kind, int rule,
                        uint8_t* q, void* scale, uint16_t* xdq, void* stream);
+
+/*
+ * fp8_block_dequantize -- block-scaled FP8 codes back to bf16.
+ *
+ * Defined by: [FP8-DSV3-ru] "Что такое FP8 простыми словами" and "Почему
+ * FP8 требует scale factors" (FP8 weights are dequantized through the
+ * block's inverse scale for higher-precision operations), "Практический
+ * смысл для инференс-инфраструктуры" (FP8 weights converted to BF16 when a
+ * backend needs it).
+ *
+ *   x = RN_bf16(RN32(decode(q) * scale))     (the fake-quant value)
+ * with scale the block's fp32 value or 2^(E-127) for an E8M0 code E.
+ * A product beyond the bf16 range rounds to +-inf (IEEE).
+ *
+ * q     [rows x cols] e4m3fn codes (16-byte aligned); NaN codes (0x7F,
+ *       0xFF), which the quantizer never writes, give NaN.
+ * scale as written by fp8_block_quantize for `kind` (uint8 E8M0 any
+ *       alignment; fp32 4-byte aligned).
+ * x     [rows x cols] bf16 out (16-byte aligned).
+ * Shape: rows, cols >= 0; cols % 32 == 0 (1x32) or cols % 128 == 0;
+ *        rows % 128 == 0 for 128x128; rows * cols / 8 <= 2^32 - 2^20.
+ */
+int fp8_block_dequantize(const uint8_t* q, const void* scale, int64_t rows, int64_t cols, int kind,
+                         uint16_t* x, void* stream);
 
 /*
  * fp8_fake_quant_merge -- QAT forward of a LoRA-adapted weight: merge

@@ -79,3 +79,30 @@ def e4m3_brute(fr):
     if a >= 448:
         best = 126
     return best | (0x80 if neg else 0)
+
+
+def rn_bf16_from_f32_bits(b):
+    """bf16 bit pattern nearest (ties to even) to the float32 with bits ``b``;
+    magnitudes that round past the largest bf16 give infinity."""
+    sign = (b >> 16) & 0x8000
+    mag = b & 0x7FFFFFFF
+    if mag == 0x7F800000:
+        return sign | 0x7F80
+    v = f32_value(mag)
+    if v == 0:
+        return sign
+    e = math.floor(math.log2(v.numerator) - math.log2(v.denominator))
+    while Fraction(2) ** e > v:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= v:
+        e += 1
+    q = max(e, -126) - 7                        # bf16 grid: 8 significant bits
+    scaled = v / (Fraction(2) ** q)
+    n = scaled.numerator // scaled.denominator
+    rem = scaled - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    val = Fraction(n) * (Fraction(2) ** q)
+    if val >= Fraction(2) ** 128:
+        return sign | 0x7F80
+    return sign | (f32_bits(float(val)) >> 16)

@@ -35,15 +35,15 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared_functions()
-    assert set(names) == {"fp8_block_quantize", "fp8_fake_quant_merge", "fp8_block_scaled_gemm",
-                          "fp8_grouped_gemm", "fp8_status_string", "fp8_abi_version"}
+    assert set(names) == {"fp8_block_quantize", "fp8_block_dequantize", "fp8_fake_quant_merge",
+                          "fp8_block_scaled_gemm", "fp8_grouped_gemm", "fp8_status_string", "fp8_abi_version"}
     raw = ctypes.CDLL(fb.library_path)
     for n in names:
         assert hasattr(raw, n), n
 
 
 def test_version_and_status_strings(lib):
-    assert lib.fp8_abi_version() == 1
+    assert lib.fp8_abi_version() == 2
     for s in range(6):
         assert len(lib.fp8_status_string(s)) > 0
     assert lib.fp8_status_string(99) == b"unknown status"
@@ -63,6 +63,22 @@ def test_quantize_validation(lib):
     assert q(A16 + 8, 4, 128, 1, 0, A16, A16, None, None) == ALIGN        # x not 16-B aligned
     assert q(A16, 4, 128, 1, 0, A16, A16 + 2, None, None) == ALIGN        # fp32 scale not 4-B aligned
     assert q(A16, 4, 128, 1, 0, A16, A16, A16 + 4, None) == ALIGN         # xdq not 16-B aligned
+
+
+def test_dequantize_validation(lib):
+    d = lib.fp8_block_dequantize
+    assert d(A16, A16, 4, 64, 7, A16, None) == INVALID             # unknown kind
+    assert d(A16, A16, 4, 48, 0, A16, None) == SHAPE               # 48 % 32
+    assert d(A16, A16, 4, 64, 1, A16, None) == SHAPE               # 64 % 128
+    assert d(A16, A16, 64, 128, 2, A16, None) == SHAPE             # rows % 128
+    assert d(A16, A16, -1, 128, 1, A16, None) == SHAPE
+    assert d(A16, A16, 1 << 22, 1 << 13, 1, A16, None) == SHAPE    # rows * cols / 8 >= 2^32
+    assert d(None, None, 0, 128, 1, None, None) == OK              # empty
+    assert d(None, A16, 4, 128, 1, A16, None) == INVALID           # null codes
+    assert d(A16, A16, 4, 128, 1, None, None) == INVALID           # null output
+    assert d(A16 + 4, A16, 4, 128, 1, A16, None) == ALIGN          # codes not 16-B aligned
+    assert d(A16, A16 + 2, 4, 128, 1, A16, None) == ALIGN          # fp32 scale not 4-B aligned
+    assert d(A16, A16, 4, 128, 1, A16 + 8, None) == ALIGN          # output not 16-B aligned
 
 
 def test_merge_validation(lib):
@@ -111,3 +127,24 @@ def test_python_binding_raises_with_status(lib):
     with pytest.raises(fb.Fp8Error) as ei:
         fb.fp8_block_quantize(x, "1x32", "ceil", q, s)
     assert ei.value.status == SHAPE
+
+
+def test_routed_expert_name_rule():
+    yes = ["model.layers.3.mlp.experts.0.gate_proj.weight",
+           "model.layers.60.mlp.experts.255.up_proj.weight",
+           "layers.1.mlp.experts.7.down_proj.weight",
+           "language_model.model.layers.12.mlp.experts.31.down_proj.weight"]
+    no = ["model.layers.3.mlp.gate.weight",                       # router
+          "model.layers.3.mlp.shared_experts.gate_proj.weight",   # shared expert
+          "model.layers.0.mlp.gate_proj.weight",                  # dense MLP
+          "model.layers.3.self_attn.q_proj.weight",
+          "model.layers.3.mlp.experts.0.gate_proj.weight_scale_inv",
+          "model.layers.3.mlp.experts.0.gate_proj.bias",
+          "model.embed_tokens.weight"]
+    assert all(fb.is_routed_expert_weight(n) for n in yes)
+    assert not any(fb.is_routed_expert_weight(n) for n in no)
+
+
+def test_quantize_state_dict_rejects_other_formats():
+    with pytest.raises(ValueError):
+        fb.quantize_state_dict({}, fmt="nvfp4")

@@ -326,3 +326,28 @@ def test_quotient_rounding_sensitive_cases():
         sb = exact.rn_f32(Fraction(amax) / 448)
         qb = exact.rn_f32(Fraction(xv) / exact.f32_value(sb))
         assert int(q[0, 1]) == exact.e4m3_brute(exact.f32_value(qb)), (amax, xv)
+
+
+def test_dequantize_every_code_exact():
+    """dequantize on arbitrary codes (every non-NaN e4m3 code) and scales
+    spanning the fp32 / E8M0 ranges, against exact rational products rounded
+    once to float32 and once to bf16."""
+    from tests.exact import e4m3_value, f32_bits, rn_bf16_from_f32_bits, rn_f32
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    q32 = np.resize(codes, (8, 256))                         # 8 rows x 256 cols
+    rng = np.random.default_rng(12)
+    e8 = np.concatenate([[0, 1, 127, 254], rng.integers(0, 255, 8 * 8 - 4)]).astype(np.uint8).reshape(8, 8)
+    f128 = np.array([[1.0, 2.0 ** -130, 3.0e38], [0.015625, 7.1e-3, 1.0e-20]] * 4, dtype=np.float32)[:, :2]
+    q128 = np.resize(codes, (128, 256))
+    f2 = np.array([[0.5, 1.7e-39]], dtype=np.float32)        # one normal, one subnormal block scale
+    cases = [(q32, e8, "1x32"), (q32, f128, "1x128"), (q128, f2, "128x128")]
+    for q, sc, kind in cases:
+        got = quant.dequantize(q, sc, kind)
+        br, bc = quant.BLOCK_SHAPE[kind]
+        for (r, c) in [(r, c) for r in range(0, q.shape[0], max(1, q.shape[0] // 16)) for c in range(q.shape[1])]:
+            sv = Fraction(2) ** (int(sc[r // br, c // bc]) - 127) if kind == "1x32" else Fraction(float(sc[r // br, c // bc]))
+            prod = e4m3_value(int(q[r, c])) * sv
+            fb = rn_f32(prod) if abs(prod) < Fraction(2) ** 128 - Fraction(2) ** 103 else (0x7F800000 | (0x80000000 if prod < 0 else 0))
+            if prod == 0 and e4m3_value(int(q[r, c])) == 0 and int(q[r, c]) & 0x80:
+                fb = 0x80000000                              # -0 * s = -0
+            assert int(got[r, c]) == rn_bf16_from_f32_bits(fb), (kind, r, c, hex(int(q[r, c])))
