@@ -288,7 +288,7 @@ WORKLOADS = {"dense": dense_workload, "mx": mx_workload, "qat": qat_workload, "p
 
 def _kernel_source_hash():
     h = hashlib.sha256()
-    for f in ("gemm.hip", "device.h", "launch.h"):
+    for f in ("gemm.hip", "device.h"):
         with open(os.path.join(HERE, "block_scaled_fp8_amax_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
