@@ -23,8 +23,10 @@ path: mx (MXFP8 quantize of W 256x512 and X 64x512, MX x MX GEMM), qat
 (LoRA merge + 128x128 fake-quant of W 7168x7168, 1x128 fake-quant of X
 8192x7168, GEMM 8192x7168x7168), prequant (MXFP8 quantization of one MoE
 layer's 256 routed experts), moe (per-token quantize of 16384x7168 and
-the grouped gate||up expert GEMM over Zipf(1.1) top-8 routing) and dequant
-(the MXFP8 MoE layer back to bf16).
+the grouped gate||up expert GEMM over Zipf(1.1) top-8 routing), moe_gather
+(the same with the routed rows read through row_index), moe_down (the
+experts' down projection, K 2048, N 7168) and dequant (the MXFP8 MoE layer
+back to bf16).
 """
 
 import argparse
@@ -280,8 +282,81 @@ def moe_workload(fb, dev):
                     cfg, "TFLOP/s")
 
 
+def moe_gather_workload(fb, dev):
+    """The MoE gate||up step without the permuted copy: per-token quantize of
+    X, then the grouped GEMM reads each routed row through row_index."""
+    import workloads
+    T, E, N, K = 16384, 256, 4096, 7168
+    tok, off = workloads.zipf_routing()
+    x = workloads.moe_tokens(dev)
+    xq = torch.empty((T, K), dtype=torch.uint8, device=dev)
+    xs = torch.empty((T, K // 128), dtype=torch.float32, device=dev)
+    idx = tok.to(torch.int32).to(dev)
+    bq = torch.empty((E, N, K), dtype=torch.uint8, device=dev)
+    sb = torch.empty((E, N, K // 32), dtype=torch.uint8, device=dev)
+    fac = workloads.expert_factors()
+    for e in range(E):
+        gate, up, _ = workloads.expert_weights(e, dev, fac)
+        fb.fp8_block_quantize(torch.cat([gate, up], 0), "1x32", "ceil", bq[e], sb[e])
+    offt = off.to(dev)
+    total_m = int(off[-1])
+    y = torch.empty((total_m, N), dtype=torch.bfloat16, device=dev)
+
+    def launches(i):
+        return [("quantize_x_1x128", lambda: fb.fp8_block_quantize(x, "1x128", "ceil", xq, xs)),
+                ("grouped_gemm_gather",
+                 lambda: fb.fp8_grouped_gemm_gather(xq, xs, "1x128", idx, bq, sb, "1x32", offt, y))]
+
+    flops = 2.0 * total_m * N * K
+    kbytes = {"quantize_x_1x128": T * K * 3 + T * (K // 128) * 4,
+              "grouped_gemm_gather": T * K + T * (K // 128) * 4 + total_m * 4 + E * N * K + E * N * (K // 32) +
+                                     total_m * N * 2 + (E + 1) * 4}
+    cfg = {"workload": "MoE gate||up with gathered rows: quantize X 16384x7168 (1x128), grouped FP8 GEMM reading "
+                       "the 131072 routed rows through row_index (Zipf(1.1) top-8, 256 experts, N 4096, K 7168, "
+                       "MXFP8 weights), bf16 out",
+           "tokens": T, "total_m": total_m, "n": N, "k": K, "groups": E}
+    return Workload(launches, "grouped_gemm_gather", "mfma", flops, sum(kbytes.values()), kbytes,
+                    {"grouped_gemm_gather": flops}, cfg, "TFLOP/s")
+
+
+def moe_down_workload(fb, dev):
+    """The MoE down projection: per-row quantize of the routed intermediate
+    activations (131072 x 2048), grouped GEMM against the experts' MXFP8
+    down weights (N 7168, K 2048)."""
+    import workloads
+    E, N, K = 256, 7168, 2048
+    tok, off = workloads.zipf_routing()
+    total_m = int(off[-1])
+    h = workloads.normal_bf16((total_m, K), 1.0, 510, dev)
+    hq = torch.empty((total_m, K), dtype=torch.uint8, device=dev)
+    hs = torch.empty((total_m, K // 128), dtype=torch.float32, device=dev)
+    bq = torch.empty((E, N, K), dtype=torch.uint8, device=dev)
+    sb = torch.empty((E, N, K // 32), dtype=torch.uint8, device=dev)
+    fac = workloads.expert_factors()
+    for e in range(E):
+        _, _, down = workloads.expert_weights(e, dev, fac)
+        fb.fp8_block_quantize(down, "1x32", "ceil", bq[e], sb[e])
+    offt = off.to(dev)
+    y = torch.empty((total_m, N), dtype=torch.bfloat16, device=dev)
+
+    def launches(i):
+        return [("quantize_h_1x128", lambda: fb.fp8_block_quantize(h, "1x128", "ceil", hq, hs)),
+                ("grouped_gemm_down", lambda: fb.fp8_grouped_gemm(hq, hs, "1x128", bq, sb, "1x32", offt, y))]
+
+    flops = 2.0 * total_m * N * K
+    kbytes = {"quantize_h_1x128": total_m * K * 3 + total_m * (K // 128) * 4,
+              "grouped_gemm_down": total_m * K + total_m * (K // 128) * 4 + E * N * K + E * N * (K // 32) +
+                                   total_m * N * 2 + (E + 1) * 4}
+    cfg = {"workload": "MoE down projection: quantize the routed intermediate 131072x2048 (1x128), grouped FP8 GEMM "
+                       "over 256 experts (Zipf(1.1) top-8, N 7168, K 2048, MXFP8 down weights), bf16 out",
+           "total_m": total_m, "n": N, "k": K, "groups": E}
+    return Workload(launches, "grouped_gemm_down", "mfma", flops, sum(kbytes.values()), kbytes,
+                    {"grouped_gemm_down": flops}, cfg, "TFLOP/s")
+
+
 WORKLOADS = {"dense": dense_workload, "mx": mx_workload, "qat": qat_workload, "prequant": prequant_workload,
-             "moe": moe_workload, "dequant": dequant_workload}
+             "moe": moe_workload, "moe_gather": moe_gather_workload, "moe_down": moe_down_workload,
+             "dequant": dequant_workload}
 
 
 # ------------------------------------------------------------ traffic record

@@ -20,7 +20,7 @@ __all__ = [
     "FP8_E8M0_CEIL", "FP8_E8M0_FLOOR", "FP8_OUT_BF16", "FP8_OUT_F32",
     "Fp8Error", "library", "library_path",
     "fp8_block_quantize", "fp8_block_dequantize", "fp8_fake_quant_merge", "fp8_block_scaled_gemm",
-    "fp8_grouped_gemm",
+    "fp8_grouped_gemm", "fp8_grouped_gemm_gather",
     "fp8_status_string", "fp8_abi_version",
     "quantize", "dequantize", "fake_quant_merge", "block_scaled_gemm", "grouped_gemm", "scale_shape",
     "is_routed_expert_weight", "quantize_state_dict",
@@ -64,6 +64,8 @@ def library():
         lib.fp8_block_scaled_gemm.restype = ci
         lib.fp8_grouped_gemm.argtypes = [vp, vp, ci, vp, vp, ci, vp, i64, i64, i64, i64, vp, ci, vp]
         lib.fp8_grouped_gemm.restype = ci
+        lib.fp8_grouped_gemm_gather.argtypes = [vp, vp, ci, i64, vp, vp, vp, ci, vp, i64, i64, i64, i64, vp, ci, vp]
+        lib.fp8_grouped_gemm_gather.restype = ci
         lib.fp8_status_string.argtypes = [ci]
         lib.fp8_status_string.restype = ctypes.c_char_p
         lib.fp8_abi_version.argtypes = []
@@ -179,6 +181,23 @@ def fp8_grouped_gemm(a_q, a_scale, a_kind, b_q, b_scale, b_kind, group_offsets, 
     _check(st, "fp8_grouped_gemm")
 
 
+def fp8_grouped_gemm_gather(a_q, a_scale, a_kind, row_index, b_q, b_scale, b_kind, group_offsets, y, stream=None):
+    """a_q [a_rows, k]; row_index int32 [total_m] on the device (A row of each
+    grouped row); b_q [groups, n, k]; group_offsets int32 [groups+1];
+    y bf16/float32 [total_m, n]."""
+    _contig(a_q, a_scale, row_index, b_q, b_scale, group_offsets, y)
+    a_rows, k = a_q.shape
+    groups, n = b_q.shape[0], b_q.shape[1]
+    if group_offsets.dtype != torch.int32 or row_index.dtype != torch.int32:
+        raise ValueError("group_offsets and row_index must be int32")
+    total_m = row_index.numel()
+    y_type = FP8_OUT_F32 if y.dtype == torch.float32 else FP8_OUT_BF16
+    st = library().fp8_grouped_gemm_gather(_ptr(a_q), _ptr(a_scale), _kind(a_kind), a_rows, _ptr(row_index),
+                                           _ptr(b_q), _ptr(b_scale), _kind(b_kind), _ptr(group_offsets), groups,
+                                           total_m, n, k, _ptr(y), y_type, _stream(stream, a_q))
+    _check(st, "fp8_grouped_gemm_gather")
+
+
 # --------------------------------------------- allocating conveniences (torch)
 
 def scale_shape(rows, cols, kind):
@@ -219,9 +238,16 @@ def block_scaled_gemm(a_q, a_scale, a_kind, b_q, b_scale, b_kind, out_dtype=torc
     return y
 
 
-def grouped_gemm(a_q, a_scale, a_kind, b_q, b_scale, b_kind, group_offsets, out_dtype=torch.bfloat16, stream=None):
-    y = torch.empty((a_q.shape[0], b_q.shape[1]), dtype=out_dtype, device=a_q.device)
-    fp8_grouped_gemm(a_q, a_scale, a_kind, b_q, b_scale, b_kind, group_offsets, y, stream)
+def grouped_gemm(a_q, a_scale, a_kind, b_q, b_scale, b_kind, group_offsets, out_dtype=torch.bfloat16, stream=None,
+                 row_index=None):
+    """Grouped GEMM; with ``row_index`` the A rows are gathered
+    (fp8_grouped_gemm_gather) and the output has row_index.numel() rows."""
+    rows = a_q.shape[0] if row_index is None else row_index.numel()
+    y = torch.empty((rows, b_q.shape[1]), dtype=out_dtype, device=a_q.device)
+    if row_index is None:
+        fp8_grouped_gemm(a_q, a_scale, a_kind, b_q, b_scale, b_kind, group_offsets, y, stream)
+    else:
+        fp8_grouped_gemm_gather(a_q, a_scale, a_kind, row_index, b_q, b_scale, b_kind, group_offsets, y, stream)
     return y
 
 

@@ -143,9 +143,10 @@ int fp8_block_scaled_gemm(const uint8_t* a_q, const void* a_scale, int a_kind, c
                                         y_type == FP8_OUT_F32, reinterpret_cast<hipStream_t>(stream)));
 }
 
-int fp8_grouped_gemm(const uint8_t* a_q, const void* a_scale, int a_kind, const uint8_t* b_q, const void* b_scale,
-                     int b_kind, const int32_t* group_offsets, int64_t groups, int64_t total_m, int64_t n, int64_t k,
-                     void* y, int y_type, void* stream) {
+static int grouped_common(const uint8_t* a_q, const void* a_scale, int a_kind, int64_t a_rows,
+                          const int32_t* row_index, bool gather, const uint8_t* b_q, const void* b_scale, int b_kind,
+                          const int32_t* group_offsets, int64_t groups, int64_t total_m, int64_t n, int64_t k, void* y,
+                          int y_type, void* stream) {
   if (!valid_kind(a_kind) || !valid_kind(b_kind)) return FP8_ERR_INVALID_ARG;
   if (y_type != FP8_OUT_BF16 && y_type != FP8_OUT_F32) return FP8_ERR_INVALID_ARG;
   if (a_kind != FP8_BLOCK_1x128_F32 || (b_kind != FP8_BLOCK_1x32_E8M0 && b_kind != FP8_BLOCK_128x128_F32))
@@ -153,16 +154,34 @@ int fp8_grouped_gemm(const uint8_t* a_q, const void* a_scale, int a_kind, const 
   if (groups < 1 || groups > 1024) return FP8_ERR_INVALID_ARG;
   if (total_m < 0 || n < 0 || k <= 0 || n % 128 || k % 128) return FP8_ERR_SHAPE;
   if (total_m > 0x7FFFFFFF || (total_m / 128 + groups) * (n / 128) > 0x7FFFFF00) return FP8_ERR_SHAPE;
+  if (gather && (a_rows < 0 || a_rows * k > 0xFFFFFFFFll)) return FP8_ERR_SHAPE;  // 32-bit row offsets
   if (total_m == 0 || n == 0) return FP8_OK;
-  if (!a_q || !a_scale || !b_q || !b_scale || !group_offsets || !y) return FP8_ERR_INVALID_ARG;
+  if (gather && a_rows == 0) return FP8_ERR_SHAPE;
+  if (!a_q || !a_scale || !b_q || !b_scale || !group_offsets || !y || (gather && !row_index))
+    return FP8_ERR_INVALID_ARG;
   if (!aligned(a_q, 16) || !aligned(b_q, 16) || !aligned(a_scale, 4) || !aligned(b_scale, 4) ||
-      !aligned(group_offsets, 4) || !aligned(y, 16))
+      !aligned(group_offsets, 4) || !aligned(y, 16) || (gather && !aligned(row_index, 4)))
     return FP8_ERR_ALIGN;
   DeviceInfo* dev = nullptr;
   if (int s = current_device(&dev)) return s;
-  return hip_status(fp8blk::launch_grouped_gemm(a_q, a_scale, a_kind, b_q, b_scale, b_kind, group_offsets, groups,
-                                                total_m, n, k, y, y_type == FP8_OUT_F32,
-                                                reinterpret_cast<hipStream_t>(stream)));
+  return hip_status(fp8blk::launch_grouped_gemm(a_q, a_scale, a_kind, gather ? row_index : nullptr, b_q, b_scale,
+                                                b_kind, group_offsets, groups, total_m, n, k, y,
+                                                y_type == FP8_OUT_F32, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int fp8_grouped_gemm(const uint8_t* a_q, const void* a_scale, int a_kind, const uint8_t* b_q, const void* b_scale,
+                     int b_kind, const int32_t* group_offsets, int64_t groups, int64_t total_m, int64_t n, int64_t k,
+                     void* y, int y_type, void* stream) {
+  return grouped_common(a_q, a_scale, a_kind, total_m, nullptr, false, b_q, b_scale, b_kind, group_offsets, groups,
+                        total_m, n, k, y, y_type, stream);
+}
+
+int fp8_grouped_gemm_gather(const uint8_t* a_q, const void* a_scale, int a_kind, int64_t a_rows,
+                            const int32_t* row_index, const uint8_t* b_q, const void* b_scale, int b_kind,
+                            const int32_t* group_offsets, int64_t groups, int64_t total_m, int64_t n, int64_t k,
+                            void* y, int y_type, void* stream) {
+  return grouped_common(a_q, a_scale, a_kind, a_rows, row_index, true, b_q, b_scale, b_kind, group_offsets, groups,
+                        total_m, n, k, y, y_type, stream);
 }
 
 }  // extern "C"

@@ -55,6 +55,7 @@ struct GemmParams {
   const void* sb;
   void* y;
   const int32_t* offsets;  // grouped only
+  const int32_t* row_index; // grouped only: A row read for each grouped row (null = the row itself)
   int64_t m, n, k;
   int64_t b_group_stride;   // bytes of B per group
   int64_t sb_group_stride;  // scale elements of B per group
@@ -255,7 +256,12 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmParams p) {
     n0 = (int64_t)tn * BN;
     mrows = (int)((p.m - m0) < BM ? (p.m - m0) : BM);
   }
-  const uint8_t* aq = p.a + m0 * K;
+  // A rows: tile row r reads row m0 + r of A, or, for a gathered grouped
+  // problem, row row_index[m0 + r] (offsets then count from A's base; the
+  // library checks that A's rows * K fit in 32 bits).
+  const bool gather = GROUPED && p.row_index != nullptr;
+  auto a_row = [&](int r) -> int64_t { return gather ? (int64_t)p.row_index[m0 + r] : (int64_t)r; };
+  const uint8_t* aq = gather ? p.a : p.a + m0 * K;
   const uint8_t* bt = bq + n0 * K;
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
 
@@ -269,7 +275,7 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmParams p) {
     for (int j = 0; j < A_PER; ++j) {
       const int r = (j * NW + wave) * 8 + sub;
       const int rr = r < mrows ? r : mrows - 1;
-      a_off[j] = (uint32_t)(rr * K) + (uint32_t)((slot ^ swz(r)) * 16);
+      a_off[j] = (uint32_t)(a_row(rr) * K) + (uint32_t)((slot ^ swz(r)) * 16);
     }
 #pragma unroll
     for (int j = 0; j < B_PER; ++j) {
@@ -287,8 +293,8 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmParams p) {
     const int r = rb * 64 + lane;
     const int rr = r < mrows ? r : mrows - 1;
     const int64_t row_bytes = A_MX ? K / 32 : (int64_t)KB * 4;
-    s_base = reinterpret_cast<const uint8_t*>(p.sa) + m0 * row_bytes;
-    s_off = (uint32_t)(rr * row_bytes);
+    s_base = reinterpret_cast<const uint8_t*>(p.sa) + (gather ? 0 : m0 * row_bytes);
+    s_off = (uint32_t)(a_row(rr) * row_bytes);
     s_lds = L::kA + L::kB + rb * 256;
   } else if constexpr (B_MX) {
     const int cb = gw % (BN / 64);
@@ -556,13 +562,14 @@ hipError_t launch_gemm(const uint8_t* a, const void* sa, int a_kind, const uint8
   return hipGetLastError();
 }
 
-hipError_t launch_grouped_gemm(const uint8_t* a, const void* sa, int a_kind, const uint8_t* b, const void* sb,
-                               int b_kind, const int32_t* offsets, int64_t groups, int64_t total_m, int64_t n,
-                               int64_t k, void* y, bool out_f32, hipStream_t stream) {
+hipError_t launch_grouped_gemm(const uint8_t* a, const void* sa, int a_kind, const int32_t* row_index,
+                               const uint8_t* b, const void* sb, int b_kind, const int32_t* offsets, int64_t groups,
+                               int64_t total_m, int64_t n, int64_t k, void* y, bool out_f32, hipStream_t stream) {
   (void)a_kind;
   GemmParams p{};
   p.a = a; p.sa = sa; p.b = b; p.sb = sb; p.y = y;
   p.offsets = offsets;
+  p.row_index = row_index;
   p.m = total_m; p.n = n; p.k = k;
   p.groups = (int)groups;
   p.b_group_stride = n * k;

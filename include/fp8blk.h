@@ -203,6 +203,31 @@ int fp8_grouped_gemm(const uint8_t* a_q, const void* a_scale, int a_kind,
                      const int32_t* group_offsets, int64_t groups, int64_t total_m,
                      int64_t n, int64_t k, void* y, int y_type, void* stream);
 
+/*
+ * fp8_grouped_gemm_gather -- fp8_grouped_gemm whose A rows are gathered.
+ *
+ * Defined by: the MoE dispatch of [DSV3-Blog5] "Reducing Communication
+ * Overhead in MoE with FP8" (routed tokens carry FP8 activations) and
+ * [FP8-DSV3-ru] "Как FP8 связан с MoE-архитектурой DeepSeek V3" (each token
+ * activates only some of the experts): each token's activations are
+ * quantized once, per token in 1x128 tiles, and every expert reads the rows
+ * of the tokens routed to it.
+ *
+ * Grouped row i (group g owns [off[g], off[g+1])) is
+ *   Y[i] = deq(A[row_index[i]]) . deq(B[g])^T,   fp32 accumulation,
+ * i.e. fp8_grouped_gemm on the rows A[row_index[0..total_m-1]], without
+ * writing that permuted copy.
+ * a_q [a_rows x k] codes, a_kind = FP8_BLOCK_1x128_F32 (float scales
+ *     [a_rows][k/128]); a_rows * k < 2^32.
+ * row_index: DEVICE int32 [total_m], values in [0, a_rows) (not checked: a
+ *     violation is undefined); 4-byte aligned.
+ * Every other argument as for fp8_grouped_gemm.
+ */
+int fp8_grouped_gemm_gather(const uint8_t* a_q, const void* a_scale, int a_kind, int64_t a_rows,
+                            const int32_t* row_index, const uint8_t* b_q, const void* b_scale, int b_kind,
+                            const int32_t* group_offsets, int64_t groups, int64_t total_m, int64_t n, int64_t k,
+                            void* y, int y_type, void* stream);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char* fp8_status_string(int status);
 

@@ -36,7 +36,8 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = _declared_functions()
     assert set(names) == {"fp8_block_quantize", "fp8_block_dequantize", "fp8_fake_quant_merge",
-                          "fp8_block_scaled_gemm", "fp8_grouped_gemm", "fp8_status_string", "fp8_abi_version"}
+                          "fp8_block_scaled_gemm", "fp8_grouped_gemm", "fp8_grouped_gemm_gather",
+                          "fp8_status_string", "fp8_abi_version"}
     raw = ctypes.CDLL(fb.library_path)
     for n in names:
         assert hasattr(raw, n), n
@@ -117,6 +118,16 @@ def test_grouped_validation(lib):
     assert g(A16, A16, 1, A16, A16, 0, A16, 4, 0, 128, 128, A16, 0, None) == OK          # no rows
     assert g(A16, A16, 1, A16, A16, 0, None, 4, 8, 128, 128, A16, 0, None) == INVALID
     assert g(A16, A16, 1, A16, A16, 0, A16 + 2, 4, 8, 128, 128, A16, 0, None) == ALIGN
+
+
+def test_grouped_gather_validation(lib):
+    g = lib.fp8_grouped_gemm_gather
+    assert g(A16, A16, 1, 16, None, A16, A16, 0, A16, 4, 8, 128, 128, A16, 0, None) == INVALID   # no row_index
+    assert g(A16, A16, 1, 16, A16 + 2, A16, A16, 0, A16, 4, 8, 128, 128, A16, 0, None) == ALIGN  # row_index 4 B
+    assert g(A16, A16, 1, 1 << 20, A16, A16, A16, 0, A16, 4, 8, 128, 1 << 13, A16, 0, None) == SHAPE  # A > 2^32 B
+    assert g(A16, A16, 1, 0, A16, A16, A16, 0, A16, 4, 8, 128, 128, A16, 0, None) == SHAPE       # no A rows
+    assert g(A16, A16, 1, 0, None, A16, A16, 0, A16, 4, 0, 128, 128, A16, 0, None) == OK          # no grouped rows
+    assert g(A16, A16, 0, 16, A16, A16, A16, 0, A16, 4, 8, 128, 128, A16, 0, None) == UNSUP       # A must be 1x128
 
 
 def test_python_binding_raises_with_status(lib):

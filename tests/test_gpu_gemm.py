@@ -220,3 +220,67 @@ def test_grouped_moe_full():
         print(f"[grouped] group {g} rows {hi - lo} err {err:.3e}", flush=True)
         assert err <= TOL
         assert np.array_equal(bf16_bits(y[rows]), codec.f32_to_bf16(got))
+
+
+# ------------------------------------------------------------ gathered rows
+
+@pytest.mark.parametrize("bkind", ["1x32", "128x128"])
+def test_grouped_gather_small(bkind):
+    """Rows gathered through row_index equal the oracle on the permuted copy
+    and, bit for bit, the plain grouped kernel run on that copy."""
+    rng = np.random.default_rng(90)
+    tokens, g, n, k, top = 300, 9, 256, 512, 2
+    experts = np.stack([rng.choice(g - 2, top, replace=False) for _ in range(tokens)])   # groups 7, 8 empty
+    flat = experts.reshape(-1)
+    tok = np.repeat(np.arange(tokens), top)
+    order = np.lexsort((tok, flat))
+    row_index = tok[order].astype(np.int32)
+    off = np.concatenate([[0], np.cumsum(np.bincount(flat, minlength=g))]).astype(np.int32)
+    aq, sa = _q(_rand_bf16((tokens, k), 1.0, 91), "1x128")
+    bq, sb = _q(_rand_bf16((g * n, k), 0.02, 92), bkind)
+    bq = bq.view(g, n, k)
+    sb = sb.view(g, n, k // 32) if bkind == "1x32" else sb.view(g, n // 128, k // 128)
+    offt = torch.from_numpy(off).cuda()
+    idx = torch.from_numpy(row_index).cuda()
+    print(f"[grouped] gather {bkind} tokens {tokens} rows {len(row_index)}", flush=True)
+    y = fb.grouped_gemm(aq, sa, "1x128", bq, sb, bkind, offt, out_dtype=torch.float32, row_index=idx)
+    y16 = fb.grouped_gemm(aq, sa, "1x128", bq, sb, bkind, offt, row_index=idx)
+    ap, sp = aq.index_select(0, idx.long()).contiguous(), sa.index_select(0, idx.long()).contiguous()
+    yp = fb.grouped_gemm(ap, sp, "1x128", bq, sb, bkind, offt, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int32), yp.view(torch.int32))
+    ref = gemm.grouped_gemm_ref(ap.cpu().numpy(), sp.cpu().numpy(), "1x128", bq.cpu().numpy(), sb.cpu().numpy(),
+                                bkind, off)
+    y32 = y.cpu().numpy()
+    for e in range(g):
+        lo, hi = off[e], off[e + 1]
+        if hi > lo:
+            assert gemm.normwise_rel_err(y32[lo:hi], ref[e]) <= TOL, e
+    assert np.array_equal(bf16_bits(y16), codec.f32_to_bf16(y32))
+
+
+def test_grouped_gather_moe_full():
+    """The MoE gate||up GEMM (131072 routed rows over 256 experts) reading the
+    16384 per-token quantized rows through row_index gives the same bytes as
+    the grouped GEMM on the materialized permuted copy."""
+    tok, off = zipf_routing()
+    x = moe_tokens("cuda")
+    xq, xs = _q(x, "1x128")
+    del x
+    fac = expert_factors()
+    bq = torch.empty((256, 4096, 7168), dtype=torch.uint8, device="cuda")
+    sb = torch.empty((256, 4096, 224), dtype=torch.uint8, device="cuda")
+    for e in range(256):
+        gate, up, _ = expert_weights(e, "cuda", fac)
+        wq, ws = _q(torch.cat([gate, up], 0), "1x32")
+        bq[e].copy_(wq)
+        sb[e].copy_(ws)
+    offt = off.cuda()
+    idx = tok.to(torch.int32).cuda()
+    print("[grouped] gather MoE 131072x4096x7168", flush=True)
+    y = fb.grouped_gemm(xq, xs, "1x128", bq, sb, "1x32", offt, row_index=idx)
+    ap = xq.index_select(0, idx.long()).contiguous()
+    sp = xs.index_select(0, idx.long()).contiguous()
+    yp = fb.grouped_gemm(ap, sp, "1x128", bq, sb, "1x32", offt)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), yp.view(torch.int16))
