@@ -166,7 +166,8 @@ static int grouped_common(const uint8_t* a_q, const void* a_scale, int a_kind, i
   if (int s = current_device(&dev)) return s;
   return hip_status(fp8blk::launch_grouped_gemm(a_q, a_scale, a_kind, gather ? row_index : nullptr, b_q, b_scale,
                                                 b_kind, group_offsets, groups, total_m, n, k, y,
-                                                y_type == FP8_OUT_F32, reinterpret_cast<hipStream_t>(stream)));
+                                                y_type == FP8_OUT_F32, dev->num_cu,
+                                                reinterpret_cast<hipStream_t>(stream)));
 }
 
 int fp8_grouped_gemm(const uint8_t* a_q, const void* a_scale, int a_kind, const uint8_t* b_q, const void* b_scale,

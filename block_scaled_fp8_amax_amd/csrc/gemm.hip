@@ -124,22 +124,18 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
   }
 }
 
-// Grouped tile order.  Every workgroup rebuilds, in LDS, the number of
+// Grouped tile order.  Every workgroup builds, in LDS, the number of
 // m-tiles of each group (ceil(M_g / BM)) and their prefix sums; the tiles
 // of group g are numbered after those of groups 0..g-1, banded inside the
-// group like the dense order.  Consecutive runs of 32 tiles ("windows",
-// one per CU of an XCD) share A rows and B columns; window w runs on XCD
+// group like the dense order.  Consecutive runs of tiles ("windows", one
+// tile per CU of an XCD) share A rows and B columns; window w runs on XCD
 // w mod 8, so each XCD sees a mix of large (compute-bound) and small
-// (memory-bound) groups.  The grid is an upper bound (total_m/BM + groups
-// m-tile slots per n-tile, rounded up to a multiple of 256); workgroups
-// whose tile index reaches the real count T return at once.
-// `scratch` is LDS of at least 2 * 1025 ints; returns false when workgroup
-// blockIdx.x has no tile.
+// (memory-bound) groups.  The grid is persistent: one workgroup per CU;
+// workgroup b (XCD b mod 8, slot b / 8) takes slot b / 8 of every window of
+// its XCD in turn.
+// s_off / s_pref: LDS of groups + 1 ints each; returns the tile count.
 template <int BM>
-__device__ __forceinline__ bool grouped_tile(const GemmParams& p, int* scratch, int nthreads, int* g_out,
-                                             int64_t* row0, int* rows, int* tn_out) {
-  int* s_off = scratch;
-  int* s_pref = scratch + 1025;
+__device__ __forceinline__ int grouped_prefix(const GemmParams& p, int* s_off, int* s_pref, int nthreads) {
   const int groups = p.groups;
   const int t = threadIdx.x;
   for (int g = t; g <= groups; g += nthreads) s_off[g] = p.offsets[g];
@@ -156,14 +152,16 @@ __device__ __forceinline__ bool grouped_tile(const GemmParams& p, int* scratch, 
     for (int g = t; g < groups; g += nthreads) s_pref[g + 1] += v[cnt++];
     __syncthreads();
   }
+  return s_pref[groups] * p.tiles_n;
+}
+
+// Tile L (< the tile count) -> group, first row, rows, n-tile.
+template <int BM>
+__device__ __forceinline__ void grouped_locate(const GemmParams& p, const int* s_off, const int* s_pref, int L,
+                                               int* g_out, int64_t* row0, int* rows, int* tn_out) {
   const int tiles_n = p.tiles_n;
-  const int T = s_pref[groups] * tiles_n;
-  const int i = (int)blockIdx.x;
-  const int j = i >> 3;                                    // index among this XCD's workgroups
-  const int L = ((((j >> 5) << 3) + (i & 7)) << 5) + (j & 31);
-  if (L >= T) return false;
   const int slot = L / tiles_n;
-  int lo = 0, hi = groups - 1;  // g with s_pref[g] <= slot < s_pref[g+1]
+  int lo = 0, hi = p.groups - 1;  // g with s_pref[g] <= slot < s_pref[g+1]
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
     if (s_pref[mid] <= slot) lo = mid; else hi = mid - 1;
@@ -181,7 +179,6 @@ __device__ __forceinline__ bool grouped_tile(const GemmParams& p, int* scratch, 
   *row0 = (int64_t)s_off[g] + (int64_t)tm * BM;
   const int64_t left = (int64_t)s_off[g + 1] - *row0;
   *rows = (int)(left < BM ? left : BM);
-  return true;
 }
 
 template <int BM, int BN, int STAGES>
@@ -222,6 +219,7 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmParams p) {
   constexpr bool B_MX = (MODE != kF32xF32);
   using L = Layout<BM, BN, STAGES>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[L::kBytes];
+  __shared__ int s_grp[GROUPED ? 2 * 1025 : 1];   // grouped: offsets and m-tile prefix
 
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -232,15 +230,22 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmParams p) {
   const int wn = grp * GNB + gw / WMB;
   const int64_t K = p.k;
   const int KB = (int)(K / kBK);
+  int n_tiles = 1;
+  if constexpr (GROUPED) n_tiles = grouped_prefix<BM>(p, s_grp, s_grp + 1025, NW * 64);
 
+  // dense: one tile per workgroup; grouped: this workgroup's tiles in turn
+  for (int it = 0;; ++it) {
   // ---- tile coordinates
   int64_t m0, n0;
   int mrows;
   const uint8_t* bq = p.b;
   const uint8_t* sb8 = reinterpret_cast<const uint8_t*>(p.sb);
   if constexpr (GROUPED) {
+    const int wsz = (int)(gridDim.x >> 3);                    // window = one tile per CU of an XCD
+    const int tile = (it * 8 + (int)(blockIdx.x & 7)) * wsz + (int)(blockIdx.x >> 3);
+    if (tile >= n_tiles) break;
     int g, tn;
-    if (!grouped_tile<BM>(p, reinterpret_cast<int*>(smem), NW * 64, &g, &m0, &mrows, &tn)) return;
+    grouped_locate<BM>(p, s_grp, s_grp + 1025, tile, &g, &m0, &mrows, &tn);
     g = __builtin_amdgcn_readfirstlane(g);
     tn = __builtin_amdgcn_readfirstlane(tn);
     m0 = (int64_t)__builtin_amdgcn_readfirstlane((int)m0);
@@ -248,8 +253,8 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmParams p) {
     n0 = (int64_t)tn * BN;
     bq += (int64_t)g * p.b_group_stride;
     sb8 += (int64_t)g * p.sb_group_stride * (B_MX ? 1 : 4);
-    __syncthreads();   // the scratch above is overwritten by the first stages
   } else {
+    if (it > 0) break;
     int tm, tn;
     dense_tile(p, &tm, &tn);
     m0 = (int64_t)tm * BM;
@@ -529,6 +534,8 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmParams p) {
       }
     }
   }
+  __syncthreads();   // the next tile's loads reuse this LDS
+  }  // tile loop
 }
 
 template <int MODE, bool GROUPED, int BM, int BN>
@@ -564,7 +571,8 @@ hipError_t launch_gemm(const uint8_t* a, const void* sa, int a_kind, const uint8
 
 hipError_t launch_grouped_gemm(const uint8_t* a, const void* sa, int a_kind, const int32_t* row_index,
                                const uint8_t* b, const void* sb, int b_kind, const int32_t* offsets, int64_t groups,
-                               int64_t total_m, int64_t n, int64_t k, void* y, bool out_f32, hipStream_t stream) {
+                               int64_t total_m, int64_t n, int64_t k, void* y, bool out_f32, int num_cu,
+                               hipStream_t stream) {
   (void)a_kind;
   GemmParams p{};
   p.a = a; p.sa = sa; p.b = b; p.sb = sb; p.y = y;
@@ -576,11 +584,10 @@ hipError_t launch_grouped_gemm(const uint8_t* a, const void* sa, int a_kind, con
   p.sb_group_stride = b_kind == 0 ? n * (k / 32) : (n / 128) * (k / 128);
   p.band = kGroupBand;
   const bool wide = n % 256 == 0;
-  const int bm = wide ? 128 : 256;
   p.tiles_n = (int)(wide ? n / 256 : n / 128);
-  const int64_t slots = total_m / bm + groups;   // >= sum over groups of ceil(M_g / bm)
-  const int64_t wgs = (slots * p.tiles_n + 255) / 256 * 256;
-  if (wgs > 0x7FFFFFFF) return hipErrorInvalidValue;
+  // persistent: one workgroup per CU (the kernel's LDS admits one), a
+  // multiple of the 8 XCDs
+  const int wgs = num_cu >= 8 ? num_cu / 8 * 8 : 8;
   dim3 grid((unsigned)wgs);
   if (b_kind == 0) {
     if (wide) launch_pp<kF32xMX, true, 128, 256>(p, grid, out_f32, stream);
