@@ -140,7 +140,7 @@ int fp8_block_scaled_gemm(const uint8_t* a_q, const void* a_scale, int a_kind, c
   DeviceInfo* dev = nullptr;
   if (int s = current_device(&dev)) return s;
   return hip_status(fp8blk::launch_gemm(a_q, a_scale, a_kind, b_q, b_scale, b_kind, m, n, k, y,
-                                        y_type == FP8_OUT_F32, reinterpret_cast<hipStream_t>(stream)));
+                                        y_type == FP8_OUT_F32, dev->num_cu, reinterpret_cast<hipStream_t>(stream)));
 }
 
 static int grouped_common(const uint8_t* a_q, const void* a_scale, int a_kind, int64_t a_rows,

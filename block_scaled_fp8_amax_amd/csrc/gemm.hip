@@ -64,15 +64,21 @@ struct GemmParams {
   int band;                 // m-tiles per band of the tile order (0 = one band)
 };
 
-// Dense tile order.  Workgroup i is dispatched to XCD i % 8 and the XCDs
-// have separate L2 caches, so consecutive tile indices are given to one XCD
-// (a contiguous range of 1/8 of the tiles each), and tiles are numbered
-// column by column inside bands of `band` m-tiles, which makes each XCD's
-// range a compact band x (range/band) block of the output.
-__device__ __forceinline__ void dense_tile(const GemmParams& p, int* tm, int* tn) {
-  const int nwg = p.tiles_m * p.tiles_n;
-  int id = blockIdx.x;
-  if ((nwg & 7) == 0) id = (id & 7) * (nwg >> 3) + (id >> 3);
+// Dense tile order.  Workgroup b runs on XCD b % 8 and the XCDs have
+// separate L2 caches, so each XCD takes a contiguous 1/8 of the tile
+// indices, handed to its workgroups in turn (slot b / 8 takes indices
+// slot, slot + W, ... of the range, W = workgroups per XCD); tiles are
+// numbered column by column inside bands of `band` m-tiles, which makes
+// the tiles an XCD runs at once a compact band x (W/band) block.
+__device__ __forceinline__ int dense_tile_id(const GemmParams& p, int it) {
+  const int T = p.tiles_m * p.tiles_n;
+  const int x = (int)(blockIdx.x & 7), wsz = (int)(gridDim.x >> 3);
+  const int q = T >> 3, rem = T & 7;
+  const int cnt = q + (x < rem ? 1 : 0), start = x * q + (x < rem ? x : rem);
+  const int j = (int)(blockIdx.x >> 3) + it * wsz;
+  return j < cnt ? start + j : -1;
+}
+__device__ __forceinline__ void dense_tile(const GemmParams& p, int id, int* tm, int* tn) {
   const int band = p.band > 0 ? p.band : p.tiles_m;
   const int per_band = band * p.tiles_n;
   const int b = id / per_band, r = id - b * per_band;
@@ -233,7 +239,7 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmParams p) {
   int n_tiles = 1;
   if constexpr (GROUPED) n_tiles = grouped_prefix<BM>(p, s_grp, s_grp + 1025, NW * 64);
 
-  // dense: one tile per workgroup; grouped: this workgroup's tiles in turn
+  // this workgroup's tiles in turn (persistent grid)
   for (int it = 0;; ++it) {
   // ---- tile coordinates
   int64_t m0, n0;
@@ -254,9 +260,10 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmParams p) {
     bq += (int64_t)g * p.b_group_stride;
     sb8 += (int64_t)g * p.sb_group_stride * (B_MX ? 1 : 4);
   } else {
-    if (it > 0) break;
+    const int id = dense_tile_id(p, it);
+    if (id < 0) break;
     int tm, tn;
-    dense_tile(p, &tm, &tn);
+    dense_tile(p, id, &tm, &tn);
     m0 = (int64_t)tm * BM;
     n0 = (int64_t)tn * BN;
     mrows = (int)((p.m - m0) < BM ? (p.m - m0) : BM);
@@ -554,14 +561,19 @@ constexpr int kDenseBand = 4;
 constexpr int kGroupBand = 8;
 
 hipError_t launch_gemm(const uint8_t* a, const void* sa, int a_kind, const uint8_t* b, const void* sb, int b_kind,
-                       int64_t m, int64_t n, int64_t k, void* y, bool out_f32, hipStream_t stream) {
+                       int64_t m, int64_t n, int64_t k, void* y, bool out_f32, int num_cu, hipStream_t stream) {
   GemmParams p{};
   p.a = a; p.sa = sa; p.b = b; p.sb = sb; p.y = y;
   p.m = m; p.n = n; p.k = k;
   p.tiles_m = (int)((m + 255) / 256);
   p.tiles_n = (int)(n / 128);
   p.band = kDenseBand;
-  dim3 grid((unsigned)(p.tiles_m * p.tiles_n));
+  // persistent: at most one workgroup per CU (the kernel's LDS admits one),
+  // a multiple of the 8 XCDs
+  const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
+  const int64_t full = num_cu >= 8 ? num_cu / 8 * 8 : 8;
+  const int64_t wgs = tiles < full ? (tiles + 7) / 8 * 8 : full;
+  dim3 grid((unsigned)wgs);
   if (a_kind == 1 && b_kind == 2)
     launch_pp<kF32xF32, false, 256, 128>(p, grid, out_f32, stream);
   else
