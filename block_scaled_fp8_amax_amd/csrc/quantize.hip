@@ -121,20 +121,20 @@ __global__ __launch_bounds__(kQRowsThreads) void quant_rows_kernel(const u32x4* 
 // 128x128 blocks: grid = (cols/128, rows/128), 256 threads.
 // Thread t covers column chunk (t % 16) * 8 of rows (t / 16) + 16 * i.
 template <bool DQ>
-__global__ __launch_bounds__(256) void quant_128_kernel(const uint16_t* __restrict__ x, int64_t cols,
+__global__ __launch_bounds__(512) void quant_128_kernel(const uint16_t* __restrict__ x, int64_t cols,
                                                         uint8_t* __restrict__ q, float* __restrict__ scale,
                                                         uint16_t* __restrict__ xdq) {
-  __shared__ uint32_t red[4];
+  __shared__ uint32_t red[8];
   const int t = threadIdx.x;
   const int64_t r0 = (int64_t)blockIdx.y * 128 + (t >> 4);
   const int64_t c0 = (int64_t)blockIdx.x * 128 + (t & 15) * 8;
-  u32x4 v[8];
+  u32x4 v[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + (r0 + 16 * i) * cols + c0));
+  for (int i = 0; i < 4; ++i)
+    v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + (r0 + 32 * i) * cols + c0));
   uint32_t m = 0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < 4; ++i) {
     const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
     const uint32_t mi = absmax_bits<4>(w);
     m = m > mi ? m : mi;
@@ -144,13 +144,13 @@ __global__ __launch_bounds__(256) void quant_128_kernel(const uint16_t* __restri
   __syncthreads();
   m = red[0];
 #pragma unroll
-  for (int i = 1; i < 4; ++i) m = m > red[i] ? m : red[i];
+  for (int i = 1; i < 8; ++i) m = m > red[i] ? m : red[i];
   const F32Block fb = f32_block(m);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < 4; ++i) {
     u32x4 dqv;
     const u32x2 c = encode_chunk<true, false, DQ>(v[i], fb, 0.f, fb.s, &dqv);
-    const int64_t off = (r0 + 16 * i) * cols + c0;
+    const int64_t off = (r0 + 32 * i) * cols + c0;
     __builtin_nontemporal_store(c, reinterpret_cast<u32x2*>(q + off));
     if constexpr (DQ) __builtin_nontemporal_store(dqv, reinterpret_cast<u32x4*>(xdq + off));
   }
@@ -205,9 +205,9 @@ hipError_t launch_quant_128(const uint16_t* x, int64_t rows, int64_t cols, uint8
                             hipStream_t stream) {
   dim3 grid((unsigned)(cols / 128), (unsigned)(rows / 128));
   if (xdq)
-    hipLaunchKernelGGL((quant_128_kernel<true>), grid, dim3(256), 0, stream, x, cols, q, scale, xdq);
+    hipLaunchKernelGGL((quant_128_kernel<true>), grid, dim3(512), 0, stream, x, cols, q, scale, xdq);
   else
-    hipLaunchKernelGGL((quant_128_kernel<false>), grid, dim3(256), 0, stream, x, cols, q, scale, xdq);
+    hipLaunchKernelGGL((quant_128_kernel<false>), grid, dim3(512), 0, stream, x, cols, q, scale, xdq);
   return hipGetLastError();
 }
 
