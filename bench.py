@@ -430,6 +430,93 @@ def cpu_baseline_dense(sample_rows=256):
                       f"{secs:.2f} s on the host"}
 
 
+def _timed(fn):
+    t0 = time.perf_counter()
+    r = fn()
+    return r, time.perf_counter() - t0
+
+
+def cpu_baseline_mx():
+    """The oracle on the whole MXFP8 small step (it is small)."""
+    import workloads
+    from oracle import gemm as ogemm, quant as oquant
+    d = workloads.mx_small("cpu")
+    wb, xb = workloads.bf16_bits(d["w"]), workloads.bf16_bits(d["x"])
+    (w, dt1) = _timed(lambda: oquant.quantize(wb, "1x32"))
+    (x, dt2) = _timed(lambda: oquant.quantize(xb, "1x32"))
+    (_, dt3) = _timed(lambda: ogemm.gemm_ref32(x[0], x[1], "1x32", w[0], w[1], "1x32"))
+    secs = dt1 + dt2 + dt3
+    return {"value": 2.0 * 64 * 256 * 512 / secs / 1e12, "unit": "TFLOP/s", "cores": _oracle_threads(),
+            "kind": "oracle", "sample": f"the whole step (quantize W and X 1x32, GEMM 64x256x512); {secs:.3f} s"}
+
+
+def cpu_baseline_qat(rows=128):
+    """The oracle on a row slice of the QAT step: merge + fake-quant of 128
+    of the 7168 weight rows, fake-quant of 128 of the 8192 activation rows,
+    and their GEMM against the full merged weight."""
+    import workloads
+    from oracle import gemm as ogemm, merge as omerge, quant as oquant
+    d = workloads.qat_forward("cpu", m=rows)
+    wb, ab, bb, xb = (workloads.bf16_bits(d[k]) for k in ("w", "lora_a", "lora_b", "x"))
+    (_, dt1) = _timed(lambda: omerge.fake_quant_merge(wb[:rows], bb[:rows], ab))
+    (x, dt2) = _timed(lambda: oquant.quantize(xb, "1x128"))
+    wq, ws, _ = oquant.quantize(wb, "128x128")             # GEMM operand (not timed)
+    (_, dt3) = _timed(lambda: ogemm.gemm_ref32(x[0], x[1], "1x128", wq, ws, "128x128"))
+    secs = dt1 + dt2 + dt3
+    return {"value": 2.0 * rows * 7168 * 7168 / secs / 1e12, "unit": "TFLOP/s", "cores": _oracle_threads(),
+            "kind": "oracle", "sample": f"merge + fake-quant of W rows 0..{rows - 1}, fake-quant of X {rows}x7168, "
+                                        f"GEMM {rows}x7168x7168 (about 1/60 of the step); {secs:.2f} s"}
+
+
+def cpu_baseline_quant_expert(dequant=False):
+    """The oracle on one expert's gate projection (2048x7168, 1x32), about
+    1/770 of the MoE layer's elements."""
+    import workloads
+    from oracle import quant as oquant
+    gate, _, _ = workloads.expert_weights(0, "cpu")
+    gb = workloads.bf16_bits(gate)
+    n = gb.size
+    if dequant:
+        q, sc, _ = oquant.quantize(gb, "1x32")
+        (_, secs) = _timed(lambda: oquant.dequantize(q, sc, "1x32"))
+        what = "dequantize"
+    else:
+        (_, secs) = _timed(lambda: oquant.quantize(gb, "1x32"))
+        what = "quantize"
+    return {"value": (n * 3 + n / 32) / secs / 1e9, "unit": "GB/s", "cores": _oracle_threads(), "kind": "oracle",
+            "sample": f"{what} of expert 0's gate projection 2048x7168 (1x32, E8M0); {secs:.2f} s"}
+
+
+def cpu_baseline_grouped(n=4096, k=7168, rows=256, down=False):
+    """The oracle on one routed slice of the grouped step: quantize 256
+    activation rows (1x128) and their GEMM against one expert's weights."""
+    import workloads
+    from oracle import gemm as ogemm, quant as oquant
+    x = workloads.normal_bf16((rows, k), 1.0, 520, "cpu", 0.01, 50.0, outlier_channels=True)
+    gate, up, dn = workloads.expert_weights(0, "cpu")
+    w = dn if down else torch.cat([gate, up], 0)
+    wq, ws, _ = oquant.quantize(workloads.bf16_bits(w), "1x32")   # expert weights (not timed)
+    (xq, dt1) = _timed(lambda: oquant.quantize(workloads.bf16_bits(x), "1x128"))
+    (_, dt2) = _timed(lambda: ogemm.grouped_gemm_ref(xq[0], xq[1], "1x128", wq[None], ws[None], "1x32",
+                                                      [0, rows]))
+    secs = dt1 + dt2
+    return {"value": 2.0 * rows * n * k / secs / 1e12, "unit": "TFLOP/s", "cores": _oracle_threads(),
+            "kind": "oracle", "sample": f"quantize {rows}x{k} (1x128) and one expert's GEMM {rows}x{n}x{k}; "
+                                        f"{secs:.2f} s"}
+
+
+CPU_BASELINES = {
+    "dense": lambda: cpu_baseline_dense(),
+    "mx": cpu_baseline_mx,
+    "qat": lambda: cpu_baseline_qat(),
+    "prequant": lambda: cpu_baseline_quant_expert(False),
+    "dequant": lambda: cpu_baseline_quant_expert(True),
+    "moe": lambda: cpu_baseline_grouped(),
+    "moe_gather": lambda: cpu_baseline_grouped(),
+    "moe_down": lambda: cpu_baseline_grouped(n=7168, k=2048, down=True),
+}
+
+
 # ---------------------------------------------------------------------- main
 
 _SPIN_PER_MS = None
@@ -543,8 +630,8 @@ def run(args):
         "components": components,
         "roofline": roof,
     }
-    if args.config == "dense" and not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline_dense()
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = CPU_BASELINES[args.config]()
     print(json.dumps(out), flush=True)
 
 
