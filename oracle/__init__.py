@@ -29,10 +29,11 @@ Modules
   quant   block amax, scale rules, quantize, dequantize (fake-quant output)
   merge   LoRA merge W + B.A in bf16 followed by 128x128 fake-quant
   gemm    block-scaled GEMM and grouped GEMM references, error metric
+  lora_grad  QAT backward for the LoRA factors (straight-through fake-quant)
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 against closed forms, brute force, torch's own dtype casts or exact
 rational arithmetic; none is "parity unpinned".
 """
 
-from . import codec, quant, merge, gemm  # noqa: F401
+from . import codec, quant, merge, gemm, lora_grad  # noqa: F401
