@@ -25,8 +25,10 @@ path: mx (MXFP8 quantize of W 256x512 and X 64x512, MX x MX GEMM), qat
 layer's 256 routed experts), moe (per-token quantize of 16384x7168 and
 the grouped gate||up expert GEMM over Zipf(1.1) top-8 routing), moe_gather
 (the same with the routed rows read through row_index), moe_down (the
-experts' down projection, K 2048, N 7168) and dequant (the MXFP8 MoE layer
-back to bf16).
+experts' down projection, K 2048, N 7168), dequant (the MXFP8 MoE layer
+back to bf16) and qat_backward (the QAT backward for the LoRA factors of the
+qat step: dB and dA from dY 8192x7168 and the fake-quantized X 8192x7168,
+rank 16).
 """
 
 import argparse
@@ -81,7 +83,7 @@ class Workload:
     """A step is a list of (name, launch) pairs; ``bytes``/``flops`` hold
     each kernel's algorithmic work per launch."""
 
-    def __init__(self, launches, dominant, bound, step_flops, step_bytes, kbytes, kflops, cfg, unit):
+    def __init__(self, launches, dominant, bound, step_flops, step_bytes, kbytes, kflops, cfg, unit, dtype="fp8"):
         self.launches = launches          # i -> [(name, fn)]
         self.dominant = dominant
         self.bound = bound                # "mfma" or "hbm"
@@ -91,6 +93,7 @@ class Workload:
         self.kflops = kflops
         self.cfg = cfg
         self.unit = unit                  # unit of ``value``
+        self.dtype = dtype                # arithmetic type of the path
 
 
 # ----------------------------------------------------------------- workloads
@@ -354,9 +357,42 @@ def moe_down_workload(fb, dev):
                     {"grouped_gemm_down": flops}, cfg, "TFLOP/s")
 
 
+def qat_backward_workload(fb, dev):
+    """QAT backward for the LoRA factors of the qat step: dB [7168 x 16] and
+    dA [16 x 7168] from the output gradient dY 8192x7168 and the
+    fake-quantized activations X_hat 8192x7168 (the 1x128 fake-quant output
+    of the forward), bf16 in and out, fp32 accumulation."""
+    import workloads
+    M, N, K, R = 8192, 7168, 7168, 16
+    nsets = _sets_for((M * N + M * K) * 2)
+    sets = []
+    for i in range(nsets):
+        d = workloads.qat_backward(dev, M, N, K, R, seed=310 + 10 * i)
+        _, _, xdq = fb.quantize(d["x"], "1x128", dequant=True)
+        sets.append((d["dy"], xdq, d["lora_b"], d["lora_a"]))
+        del d
+    ws = torch.empty(fb.fp8_lora_backward_workspace(M, N, K, R), dtype=torch.uint8, device=dev)
+    db = torch.empty((N, R), dtype=torch.bfloat16, device=dev)
+    da = torch.empty((R, K), dtype=torch.bfloat16, device=dev)
+
+    def launches(i):
+        dy, x, b, a = sets[i % nsets]
+        return [("lora_backward", lambda: fb.fp8_lora_backward(dy, x, b, a, ws, db, da))]
+
+    # algorithmic bytes: dY and X_hat once, the factors, the two gradients
+    kbytes = {"lora_backward": (M * N + M * K) * 2 + 2 * (N * R + R * K) * 2}
+    flops = 4.0 * M * R * (N + K)       # P, Q, dB and dA: 2*M*R*K + 2*M*R*N + 2*M*R*N + 2*M*R*K
+    cfg = {"workload": "QAT backward for the LoRA factors: dB = dY^T (X_hat A^T), dA = (dY B)^T X_hat with dY "
+                       "8192x7168, X_hat 8192x7168 (1x128 fake-quant of X), rank 16, bf16 in/out, fp32 accumulation",
+           "m": M, "n": N, "k": K, "rank": R, "input_sets": nsets,
+           "workspace_bytes": int(ws.numel())}
+    return Workload(launches, "lora_backward", "hbm", flops, sum(kbytes.values()), kbytes, {}, cfg, "GB/s",
+                    dtype="bf16")
+
+
 WORKLOADS = {"dense": dense_workload, "mx": mx_workload, "qat": qat_workload, "prequant": prequant_workload,
              "moe": moe_workload, "moe_gather": moe_gather_workload, "moe_down": moe_down_workload,
-             "dequant": dequant_workload}
+             "dequant": dequant_workload, "qat_backward": qat_backward_workload}
 
 
 # ------------------------------------------------------------ traffic record
@@ -505,6 +541,20 @@ def cpu_baseline_grouped(n=4096, k=7168, rows=256, down=False):
                                         f"{secs:.2f} s"}
 
 
+def cpu_baseline_qat_backward(rows=2048):
+    """The oracle on a token slice of the QAT backward: dB and dA from 2048
+    of the 8192 token rows of dY and X_hat (every column)."""
+    import workloads
+    from oracle import lora_grad
+    d = workloads.qat_backward("cpu", m=rows)
+    bits = [workloads.bf16_bits(d[k]) for k in ("dy", "x", "lora_b", "lora_a")]
+    (_, secs) = _timed(lambda: lora_grad.lora_grads(*bits))
+    nbytes = rows * (7168 + 7168) * 2 + 2 * (7168 * 16 + 16 * 7168) * 2
+    return {"value": nbytes / secs / 1e9, "unit": "GB/s", "cores": _oracle_threads(), "kind": "oracle",
+            "sample": f"dB, dA from {rows} of the 8192 token rows (1/{8192 // rows} of the step), float64 with dW "
+                      f"formed; {secs:.2f} s"}
+
+
 CPU_BASELINES = {
     "dense": lambda: cpu_baseline_dense(),
     "mx": cpu_baseline_mx,
@@ -514,6 +564,7 @@ CPU_BASELINES = {
     "moe": lambda: cpu_baseline_grouped(),
     "moe_gather": lambda: cpu_baseline_grouped(),
     "moe_down": lambda: cpu_baseline_grouped(n=7168, k=2048, down=True),
+    "qat_backward": lambda: cpu_baseline_qat_backward(),
 }
 
 
@@ -624,7 +675,7 @@ def run(args):
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms_per_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "fp8",
+        "dtype": wl.dtype,
         "data": "synthetic (seeded N(0,0.02) weights, N(0,1) activations with 1% channels x50)",
         "config": wl.cfg,
         "components": components,

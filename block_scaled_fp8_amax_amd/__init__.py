@@ -20,9 +20,9 @@ __all__ = [
     "FP8_E8M0_CEIL", "FP8_E8M0_FLOOR", "FP8_OUT_BF16", "FP8_OUT_F32",
     "Fp8Error", "library", "library_path",
     "fp8_block_quantize", "fp8_block_dequantize", "fp8_fake_quant_merge", "fp8_block_scaled_gemm",
-    "fp8_grouped_gemm", "fp8_grouped_gemm_gather",
+    "fp8_grouped_gemm", "fp8_grouped_gemm_gather", "fp8_lora_backward", "fp8_lora_backward_workspace",
     "fp8_status_string", "fp8_abi_version",
-    "quantize", "dequantize", "fake_quant_merge", "block_scaled_gemm", "grouped_gemm", "scale_shape",
+    "quantize", "dequantize", "fake_quant_merge", "block_scaled_gemm", "grouped_gemm", "lora_backward", "scale_shape",
     "is_routed_expert_weight", "quantize_state_dict",
 ]
 
@@ -30,7 +30,7 @@ FP8_OK = 0
 FP8_BLOCK_1x32_E8M0, FP8_BLOCK_1x128_F32, FP8_BLOCK_128x128_F32 = 0, 1, 2
 FP8_E8M0_CEIL, FP8_E8M0_FLOOR = 0, 1
 FP8_OUT_BF16, FP8_OUT_F32 = 0, 1
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 _KIND_NAMES = {"1x32": FP8_BLOCK_1x32_E8M0, "1x128": FP8_BLOCK_1x128_F32, "128x128": FP8_BLOCK_128x128_F32}
 _RULE_NAMES = {"ceil": FP8_E8M0_CEIL, "floor": FP8_E8M0_FLOOR}
@@ -66,6 +66,10 @@ def library():
         lib.fp8_grouped_gemm.restype = ci
         lib.fp8_grouped_gemm_gather.argtypes = [vp, vp, ci, i64, vp, vp, vp, ci, vp, i64, i64, i64, i64, vp, ci, vp]
         lib.fp8_grouped_gemm_gather.restype = ci
+        lib.fp8_lora_backward.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, vp, ctypes.c_size_t, vp, vp, ci, vp]
+        lib.fp8_lora_backward.restype = ci
+        lib.fp8_lora_backward_workspace.argtypes = [i64, i64, i64, i64, ctypes.POINTER(ctypes.c_size_t)]
+        lib.fp8_lora_backward_workspace.restype = ci
         lib.fp8_status_string.argtypes = [ci]
         lib.fp8_status_string.restype = ctypes.c_char_p
         lib.fp8_abi_version.argtypes = []
@@ -123,7 +127,7 @@ def _contig(*ts):
             raise ValueError("fp8blk expects contiguous tensors")
 
 
-# ------------------------------------------------------------ the four calls
+# ------------------------------------------------------------- entry points
 
 def fp8_block_quantize(x, kind, rule, q, scale, xdq=None, stream=None):
     """x: bf16 [rows, cols]; q: uint8/float8_e4m3fn [rows, cols]; scale: uint8
@@ -198,6 +202,33 @@ def fp8_grouped_gemm_gather(a_q, a_scale, a_kind, row_index, b_q, b_scale, b_kin
     _check(st, "fp8_grouped_gemm_gather")
 
 
+def fp8_lora_backward_workspace(m, n, k, r):
+    """Workspace bytes fp8_lora_backward needs for these sizes."""
+    out = ctypes.c_size_t(0)
+    _check(library().fp8_lora_backward_workspace(m, n, k, r, ctypes.byref(out)), "fp8_lora_backward_workspace")
+    return out.value
+
+
+def fp8_lora_backward(dy, x, lora_b, lora_a, workspace, d_lora_b, d_lora_a, stream=None):
+    """dy bf16 [m, n]; x bf16 [m, k] (the fake-quantized activations);
+    lora_b bf16 [n, r]; lora_a bf16 [r, k]; workspace uint8 device tensor of
+    at least fp8_lora_backward_workspace(m, n, k, r) bytes; d_lora_b [n, r]
+    and d_lora_a [r, k] outputs, both bf16 or both float32."""
+    _contig(dy, x, lora_b, lora_a, workspace, d_lora_b, d_lora_a)
+    m, n = dy.shape
+    k = x.shape[1]
+    r = lora_a.shape[0]
+    if x.shape[0] != m or lora_b.shape != (n, r) or lora_a.shape != (r, k):
+        raise ValueError("fp8_lora_backward: inconsistent shapes")
+    if d_lora_b.dtype != d_lora_a.dtype:
+        raise ValueError("fp8_lora_backward: both gradients must have one dtype")
+    out_type = FP8_OUT_F32 if d_lora_b.dtype == torch.float32 else FP8_OUT_BF16
+    st = library().fp8_lora_backward(_ptr(dy), _ptr(x), _ptr(lora_b), _ptr(lora_a), m, n, k, r, _ptr(workspace),
+                                     workspace.numel() * workspace.element_size(), _ptr(d_lora_b), _ptr(d_lora_a),
+                                     out_type, _stream(stream, dy))
+    _check(st, "fp8_lora_backward")
+
+
 # --------------------------------------------- allocating conveniences (torch)
 
 def scale_shape(rows, cols, kind):
@@ -249,6 +280,20 @@ def grouped_gemm(a_q, a_scale, a_kind, b_q, b_scale, b_kind, group_offsets, out_
     else:
         fp8_grouped_gemm_gather(a_q, a_scale, a_kind, row_index, b_q, b_scale, b_kind, group_offsets, y, stream)
     return y
+
+
+def lora_backward(dy, x, lora_b, lora_a, out_dtype=torch.bfloat16, workspace=None, stream=None):
+    """Allocate (dB, dA) and, unless given, the workspace, and run
+    fp8_lora_backward: returns (d_lora_b [n, r], d_lora_a [r, k])."""
+    m, n = dy.shape
+    k = x.shape[1]
+    r = lora_a.shape[0]
+    if workspace is None:
+        workspace = torch.empty(fp8_lora_backward_workspace(m, n, k, r), dtype=torch.uint8, device=dy.device)
+    db = torch.empty((n, r), dtype=out_dtype, device=dy.device)
+    da = torch.empty((r, k), dtype=out_dtype, device=dy.device)
+    fp8_lora_backward(dy, x, lora_b, lora_a, workspace, db, da, stream)
+    return db, da
 
 
 def dequantize(q, scale, block, stream=None):

@@ -185,4 +185,40 @@ int fp8_grouped_gemm_gather(const uint8_t* a_q, const void* a_scale, int a_kind,
                         total_m, n, k, y, y_type, stream);
 }
 
+static int lora_shape(int64_t m, int64_t n, int64_t k, int64_t r) {
+  if (r < 1 || r > 64) return FP8_ERR_INVALID_ARG;
+  if (m < 0 || n < 0 || k < 0 || n % 128 || k % 128) return FP8_ERR_SHAPE;
+  if (m > 0x7FFFFFFFll - 64 || n > (int64_t(1) << 24) || k > (int64_t(1) << 24)) return FP8_ERR_SHAPE;
+  return FP8_OK;
+}
+
+int fp8_lora_backward_workspace(int64_t m, int64_t n, int64_t k, int64_t r, size_t* bytes) {
+  if (!bytes) return FP8_ERR_INVALID_ARG;
+  if (int s = lora_shape(m, n, k, r)) return s;
+  *bytes = (size_t)fp8blk::lora_bwd_workspace_bytes(m, n, k, r);
+  return FP8_OK;
+}
+
+int fp8_lora_backward(const uint16_t* dy, const uint16_t* x, const uint16_t* lora_b, const uint16_t* lora_a,
+                      int64_t m, int64_t n, int64_t k, int64_t r, void* workspace, size_t workspace_bytes,
+                      void* d_lora_b, void* d_lora_a, int out_type, void* stream) {
+  if (out_type != FP8_OUT_BF16 && out_type != FP8_OUT_F32) return FP8_ERR_INVALID_ARG;
+  if (int s = lora_shape(m, n, k, r)) return s;
+  if (n == 0 && k == 0) return FP8_OK;
+  if (!workspace || (n > 0 && (!lora_b || !d_lora_b)) || (k > 0 && (!lora_a || !d_lora_a)) ||
+      (m > 0 && ((n > 0 && !dy) || (k > 0 && !x))))
+    return FP8_ERR_INVALID_ARG;
+  if (workspace_bytes < (size_t)fp8blk::lora_bwd_workspace_bytes(m, n, k, r)) return FP8_ERR_INVALID_ARG;
+  const uintptr_t oa = out_type == FP8_OUT_F32 ? 4 : 2;
+  if ((dy && !aligned(dy, 16)) || (x && !aligned(x, 16)) || (lora_a && !aligned(lora_a, 16)) ||
+      (lora_b && !aligned(lora_b, 2)) ||
+      !aligned(workspace, 256) || (d_lora_b && !aligned(d_lora_b, oa)) || (d_lora_a && !aligned(d_lora_a, oa)))
+    return FP8_ERR_ALIGN;
+  DeviceInfo* dev = nullptr;
+  if (int s = current_device(&dev)) return s;
+  return hip_status(fp8blk::launch_lora_bwd(dy, x, lora_b, lora_a, m, n, k, r, workspace, d_lora_b, d_lora_a,
+                                            out_type == FP8_OUT_F32, dev->num_cu,
+                                            reinterpret_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

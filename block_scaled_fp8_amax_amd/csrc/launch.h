@@ -22,4 +22,9 @@ hipError_t launch_grouped_gemm(const uint8_t* a, const void* sa, int a_kind, con
                                int64_t total_m, int64_t n, int64_t k, void* y, bool out_f32, int num_cu,
                                hipStream_t stream);
 
+int64_t lora_bwd_workspace_bytes(int64_t m, int64_t n, int64_t k, int64_t r);
+hipError_t launch_lora_bwd(const uint16_t* dy, const uint16_t* x, const uint16_t* lb, const uint16_t* la, int64_t m,
+                           int64_t n, int64_t k, int64_t r, void* workspace, void* d_b, void* d_a, bool out_f32,
+                           int num_cu, hipStream_t stream);
+
 }  // namespace fp8blk

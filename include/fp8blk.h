@@ -40,13 +40,14 @@
 #ifndef FP8BLK_H
 #define FP8BLK_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
 #endif
 
-#define FP8BLK_ABI_VERSION 2
+#define FP8BLK_ABI_VERSION 3
 
 typedef enum {
   FP8_OK = 0,
@@ -227,6 +228,44 @@ int fp8_grouped_gemm_gather(const uint8_t* a_q, const void* a_scale, int a_kind,
                             const int32_t* row_index, const uint8_t* b_q, const void* b_scale, int b_kind,
                             const int32_t* group_offsets, int64_t groups, int64_t total_m, int64_t n, int64_t k,
                             void* y, int y_type, void* stream);
+
+/*
+ * fp8_lora_backward -- QAT backward for the LoRA factors.
+ *
+ * Defined by: [Fireworks-QAT] Synopsis and Interpretation (QAT trains the
+ * LoRA factors in bf16 while the forward pass uses the fake-quantized
+ * merged weight and activations).  The gradient rule is not printed there;
+ * the fake-quant is taken as straight-through (identity Jacobian), so with
+ * the forward Y = X_hat . W_hat^T, W_hat = fakequant(W + B.A):
+ *   dW = dY^T . X_hat,   dB = dW . A^T,   dA = B^T . dW,
+ * computed without forming dW as dB = dY^T . (X_hat . A^T) and
+ * dA = (dY . B)^T . X_hat, products of bf16 values accumulated in fp32;
+ * the rank-r intermediates are carried as the sum of two bf16 values
+ * (16 significant bits).  Results are rounded once (RN_bf16) or kept fp32.
+ *
+ * dy     [m x n] bf16 output gradient (16-byte aligned);
+ * x      [m x k] bf16 fake-quantized activations X_hat (16-byte aligned);
+ * lora_b [n x r] bf16 (2-byte aligned); lora_a [r x k] bf16 (16-byte
+ *        aligned);
+ * workspace: DEVICE scratch of at least the size fp8_lora_backward_workspace
+ *        reports for (m, n, k, r), 256-byte aligned, owned by the caller;
+ *        its contents on entry do not matter and are garbage on exit;
+ *        concurrent calls need separate workspaces;
+ * d_lora_b [n x r], d_lora_a [r x k] out: bf16 (out_type FP8_OUT_BF16,
+ *        2-byte aligned) or float (FP8_OUT_F32, 4-byte aligned).  m == 0
+ *        writes zeros.  dy and x may be NULL when m == 0; lora_b and
+ *        d_lora_b when n == 0; lora_a and d_lora_a when k == 0.
+ * Shape: m >= 0, m < 2^31 - 64; n % 128 == 0, k % 128 == 0, n, k <= 2^24;
+ *        1 <= r <= 64.  n == k == 0 enqueues nothing.
+ */
+int fp8_lora_backward(const uint16_t* dy, const uint16_t* x, const uint16_t* lora_b,
+                      const uint16_t* lora_a, int64_t m, int64_t n, int64_t k, int64_t r,
+                      void* workspace, size_t workspace_bytes, void* d_lora_b, void* d_lora_a,
+                      int out_type, void* stream);
+
+/* Workspace bytes fp8_lora_backward needs for (m, n, k, r), into *bytes
+ * (host pointer).  Same shape checks and status codes as the call itself. */
+int fp8_lora_backward_workspace(int64_t m, int64_t n, int64_t k, int64_t r, size_t* bytes);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char* fp8_status_string(int status);

@@ -37,6 +37,7 @@ def test_exports_every_declared_symbol(lib):
     names = _declared_functions()
     assert set(names) == {"fp8_block_quantize", "fp8_block_dequantize", "fp8_fake_quant_merge",
                           "fp8_block_scaled_gemm", "fp8_grouped_gemm", "fp8_grouped_gemm_gather",
+                          "fp8_lora_backward", "fp8_lora_backward_workspace",
                           "fp8_status_string", "fp8_abi_version"}
     raw = ctypes.CDLL(fb.library_path)
     for n in names:
@@ -44,7 +45,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.fp8_abi_version() == 2
+    assert lib.fp8_abi_version() == 3
     for s in range(6):
         assert len(lib.fp8_status_string(s)) > 0
     assert lib.fp8_status_string(99) == b"unknown status"
@@ -128,6 +129,53 @@ def test_grouped_gather_validation(lib):
     assert g(A16, A16, 1, 0, A16, A16, A16, 0, A16, 4, 8, 128, 128, A16, 0, None) == SHAPE       # no A rows
     assert g(A16, A16, 1, 0, None, A16, A16, 0, A16, 4, 0, 128, 128, A16, 0, None) == OK          # no grouped rows
     assert g(A16, A16, 0, 16, A16, A16, A16, 0, A16, 4, 8, 128, 128, A16, 0, None) == UNSUP       # A must be 1x128
+
+
+def test_lora_backward_workspace(lib):
+    out = ctypes.c_size_t(0)
+    w = lib.fp8_lora_backward_workspace
+    assert w(64, 256, 384, 16, None) == INVALID
+    assert w(64, 256, 384, 0, ctypes.byref(out)) == INVALID            # rank 0
+    assert w(64, 256, 384, 65, ctypes.byref(out)) == INVALID           # rank > 64
+    assert w(64, 200, 384, 16, ctypes.byref(out)) == SHAPE
+    assert w(-1, 256, 384, 16, ctypes.byref(out)) == SHAPE
+    assert w(64, 256, 1 << 25, 16, ctypes.byref(out)) == SHAPE
+    assert w(64, 256, 384, 16, ctypes.byref(out)) == OK
+    small = out.value
+    assert small > 0 and small % 256 == 0
+    assert w(8192, 7168, 7168, 16, ctypes.byref(out)) == OK
+    assert small < out.value < 64 << 20                                 # a few MiB at the full QAT size
+    assert w(8192, 7168, 7168, 64, ctypes.byref(out)) == OK and out.value < 256 << 20
+    assert w(0, 256, 384, 16, ctypes.byref(out)) == OK and out.value > 0
+
+
+def test_lora_backward_validation(lib):
+    b = lib.fp8_lora_backward
+    need = ctypes.c_size_t(0)
+    assert lib.fp8_lora_backward_workspace(64, 256, 384, 16, ctypes.byref(need)) == OK
+    ws = need.value
+    args = [A16, A16, A16, A16, 64, 256, 384, 16, A16, ws, A16, A16, 0, None]
+
+    def call(**kw):
+        a = list(args)
+        names = ["dy", "x", "lb", "la", "m", "n", "k", "r", "wsp", "wsb", "db", "da", "out", "st"]
+        for key, v in kw.items():
+            a[names.index(key)] = v
+        return b(*a)
+
+    assert call(out=2) == INVALID                                      # unknown output type
+    assert call(r=0) == INVALID and call(r=65) == INVALID
+    assert call(n=100) == SHAPE and call(k=64) == SHAPE and call(m=-1) == SHAPE
+    assert call(n=0, k=0, dy=None, x=None, lb=None, la=None, wsp=None, db=None, da=None) == OK
+    assert call(wsp=None) == INVALID
+    assert call(wsb=ws - 1) == INVALID                                 # workspace too small
+    assert call(dy=None) == INVALID and call(x=None) == INVALID
+    assert call(lb=None) == INVALID and call(da=None) == INVALID
+    assert call(dy=A16 + 8) == ALIGN and call(x=A16 + 2) == ALIGN
+    assert call(la=A16 + 4) == ALIGN and call(lb=A16 + 1) == ALIGN
+    assert call(wsp=A16 + 128) == ALIGN                                 # workspace: 256 B
+    assert call(db=A16 + 2, out=1) == ALIGN                             # fp32 gradients: 4 B
+    assert call(db=A16 + 1) == ALIGN
 
 
 def test_python_binding_raises_with_status(lib):

@@ -87,6 +87,18 @@ def qat_forward(device="cpu", m=8192, n=HIDDEN, k=HIDDEN, r=16):
     return {"w": w, "lora_a": a, "lora_b": b, "x": x}
 
 
+def qat_backward(device="cpu", m=8192, n=HIDDEN, k=HIDDEN, r=16, seed=310):
+    """QAT backward for the LoRA factors: output gradient dY [m, n]
+    N(0, 1e-3^2); activations X [m, k] as the dense projection (the caller
+    fake-quantizes them when it wants X_hat); LoRA A [r, k], B [n, r]
+    N(0, 0.01^2)."""
+    dy = normal_bf16((m, n), 1e-3, seed, device)
+    x = normal_bf16((m, k), 1.0, seed + 1, device, 0.01, 50.0, outlier_channels=True)
+    a = normal_bf16((r, k), 0.01, seed + 2, device)
+    b = normal_bf16((n, r), 0.01, seed + 3, device)
+    return {"dy": dy, "x": x, "lora_a": a, "lora_b": b}
+
+
 def expert_factors(n_experts=N_EXPERTS):
     """Per-expert scale c_e drawn log-uniform in [0.5, 2] (seed 400, float64)."""
     rng = np.random.default_rng(400)
