@@ -21,8 +21,9 @@ Pages (titles as they appear in the source text):
   [prequant]       "fireworks-prequant 0.1.0" (PyPI page), sections
                    "Quick start", "Formats".
 
-Numeric facts the pages only name (the e4m3fn layout, E8M0) come from the
-public OCP 8-bit floating point and Microscaling (MX) specifications.
+Numeric facts the pages only name (the e4m3fn layout, E8M0, the E2M1 FP4
+element) come from the public OCP 8-bit floating point and Microscaling (MX)
+specifications.
 
 Modules
   codec   e4m3fn / E8M0 / bf16 encode and decode
@@ -30,10 +31,11 @@ Modules
   merge   LoRA merge W + B.A in bf16 followed by 128x128 fake-quant
   gemm    block-scaled GEMM and grouped GEMM references, error metric
   lora_grad  QAT backward for the LoRA factors (straight-through fake-quant)
+  nvfp4   NVFP4 prequant: E2M1 codes, e4m3 1x16 block scales, per-tensor fp32 scale
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 against closed forms, brute force, torch's own dtype casts or exact
 rational arithmetic; none is "parity unpinned".
 """
 
-from . import codec, quant, merge, gemm, lora_grad  # noqa: F401
+from . import codec, quant, merge, gemm, lora_grad, nvfp4  # noqa: F401
