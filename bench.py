@@ -26,9 +26,10 @@ layer's 256 routed experts), moe (per-token quantize of 16384x7168 and
 the grouped gate||up expert GEMM over Zipf(1.1) top-8 routing), moe_gather
 (the same with the routed rows read through row_index), moe_down (the
 experts' down projection, K 2048, N 7168), dequant (the MXFP8 MoE layer
-back to bf16) and qat_backward (the QAT backward for the LoRA factors of the
+back to bf16), qat_backward (the QAT backward for the LoRA factors of the
 qat step: dB and dA from dY 8192x7168 and the fake-quantized X 8192x7168,
-rank 16).
+rank 16) and prequant_nvfp4 (NVFP4 prequantization of the MoE layer's 256
+routed experts, one fp32 scale per expert projection).
 """
 
 import argparse
@@ -357,6 +358,48 @@ def moe_down_workload(fb, dev):
                     {"grouped_gemm_down": flops}, cfg, "TFLOP/s")
 
 
+def prequant_nvfp4_workload(fb, dev):
+    """NVFP4 prequant of one MoE layer's 256 routed experts, stacked per
+    shape as for MXFP8; every expert projection (gate, up, down) is its own
+    tensor with its own amax and fp32 scale."""
+    import workloads
+    E, I, H = 256, 2048, 7168
+    fac = workloads.expert_factors()
+    gu = torch.empty((E * 2 * I, H), dtype=torch.bfloat16, device=dev)
+    dn = torch.empty((E * H, I), dtype=torch.bfloat16, device=dev)
+    for e in range(E):
+        gate, up, down = workloads.expert_weights(e, dev, fac)
+        gu[e * 2 * I:e * 2 * I + I].copy_(gate)
+        gu[e * 2 * I + I:(e + 1) * 2 * I].copy_(up)
+        dn[e * H:(e + 1) * H].copy_(down)
+        del gate, up, down
+    guq = torch.empty((gu.shape[0], H // 2), dtype=torch.uint8, device=dev)
+    gus = torch.empty((gu.shape[0], H // 16), dtype=torch.uint8, device=dev)
+    gug = torch.empty((2 * E,), dtype=torch.float32, device=dev)
+    gua = torch.empty((2 * E,), dtype=torch.float32, device=dev)
+    dnq = torch.empty((dn.shape[0], I // 2), dtype=torch.uint8, device=dev)
+    dns = torch.empty((dn.shape[0], I // 16), dtype=torch.uint8, device=dev)
+    dng = torch.empty((E,), dtype=torch.float32, device=dev)
+    dna = torch.empty((E,), dtype=torch.float32, device=dev)
+
+    def launches(i):
+        return [("nvfp4_gate_up", lambda: fb.fp8_nvfp4_quantize(gu, I, guq, gus, gug, gua)),
+                ("nvfp4_down", lambda: fb.fp8_nvfp4_quantize(dn, H, dnq, dns, dng, dna))]
+
+    # algorithmic bytes: bf16 read once, packed codes (1/2 B) and block scales
+    # (1/16 B) written, per element; the per-tensor amax is a second read of
+    # each tensor that the algorithm's two-level scale needs
+    n_gu, n_dn = gu.numel(), dn.numel()
+    kbytes = {"nvfp4_gate_up": n_gu * 2 + n_gu // 2 + n_gu // 16 + 2 * E * 8,
+              "nvfp4_down": n_dn * 2 + n_dn // 2 + n_dn // 16 + E * 8}
+    cfg = {"workload": "NVFP4 prequant of one MoE layer: 256 experts x {gate, up 2048x7168; down 7168x2048} bf16 "
+                       "(22.5 GB) -> packed E2M1 codes + e4m3 1x16 block scales + one fp32 scale per expert "
+                       "projection (768 tensors); experts stacked per shape, one call per shape",
+           "experts": E, "elements": n_gu + n_dn, "tensors": 3 * E}
+    return Workload(launches, "nvfp4_gate_up", "hbm", 0.0, sum(kbytes.values()), kbytes, {}, cfg, "GB/s",
+                    dtype="fp4")
+
+
 def qat_backward_workload(fb, dev):
     """QAT backward for the LoRA factors of the qat step: dB [7168 x 16] and
     dA [16 x 7168] from the output gradient dY 8192x7168 and the
@@ -392,7 +435,8 @@ def qat_backward_workload(fb, dev):
 
 WORKLOADS = {"dense": dense_workload, "mx": mx_workload, "qat": qat_workload, "prequant": prequant_workload,
              "moe": moe_workload, "moe_gather": moe_gather_workload, "moe_down": moe_down_workload,
-             "dequant": dequant_workload, "qat_backward": qat_backward_workload}
+             "dequant": dequant_workload, "qat_backward": qat_backward_workload,
+             "prequant_nvfp4": prequant_nvfp4_workload}
 
 
 # ------------------------------------------------------------ traffic record
@@ -555,6 +599,19 @@ def cpu_baseline_qat_backward(rows=2048):
                       f"formed; {secs:.2f} s"}
 
 
+def cpu_baseline_nvfp4():
+    """The oracle on one expert's gate projection (2048x7168), about 1/768
+    of the MoE layer's elements."""
+    import workloads
+    from oracle import nvfp4 as onv
+    gate, _, _ = workloads.expert_weights(0, "cpu")
+    gb = workloads.bf16_bits(gate)
+    n = gb.size
+    (_, secs) = _timed(lambda: onv.quantize(gb))
+    return {"value": (n * 2 + n / 2 + n / 16) / secs / 1e9, "unit": "GB/s", "cores": _oracle_threads(),
+            "kind": "oracle", "sample": f"NVFP4 quantize of expert 0's gate projection 2048x7168; {secs:.2f} s"}
+
+
 CPU_BASELINES = {
     "dense": lambda: cpu_baseline_dense(),
     "mx": cpu_baseline_mx,
@@ -565,6 +622,7 @@ CPU_BASELINES = {
     "moe_gather": lambda: cpu_baseline_grouped(),
     "moe_down": lambda: cpu_baseline_grouped(n=7168, k=2048, down=True),
     "qat_backward": lambda: cpu_baseline_qat_backward(),
+    "prequant_nvfp4": cpu_baseline_nvfp4,
 }
 
 

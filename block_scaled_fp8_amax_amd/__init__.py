@@ -21,8 +21,10 @@ __all__ = [
     "Fp8Error", "library", "library_path",
     "fp8_block_quantize", "fp8_block_dequantize", "fp8_fake_quant_merge", "fp8_block_scaled_gemm",
     "fp8_grouped_gemm", "fp8_grouped_gemm_gather", "fp8_lora_backward", "fp8_lora_backward_workspace",
+    "fp8_nvfp4_quantize", "fp8_nvfp4_dequantize",
     "fp8_status_string", "fp8_abi_version",
-    "quantize", "dequantize", "fake_quant_merge", "block_scaled_gemm", "grouped_gemm", "lora_backward", "scale_shape",
+    "quantize", "dequantize", "fake_quant_merge", "block_scaled_gemm", "grouped_gemm", "lora_backward", "nvfp4_quantize", "nvfp4_dequantize",
+    "scale_shape",
     "is_routed_expert_weight", "quantize_state_dict",
 ]
 
@@ -30,7 +32,7 @@ FP8_OK = 0
 FP8_BLOCK_1x32_E8M0, FP8_BLOCK_1x128_F32, FP8_BLOCK_128x128_F32 = 0, 1, 2
 FP8_E8M0_CEIL, FP8_E8M0_FLOOR = 0, 1
 FP8_OUT_BF16, FP8_OUT_F32 = 0, 1
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 _KIND_NAMES = {"1x32": FP8_BLOCK_1x32_E8M0, "1x128": FP8_BLOCK_1x128_F32, "128x128": FP8_BLOCK_128x128_F32}
 _RULE_NAMES = {"ceil": FP8_E8M0_CEIL, "floor": FP8_E8M0_FLOOR}
@@ -70,6 +72,10 @@ def library():
         lib.fp8_lora_backward.restype = ci
         lib.fp8_lora_backward_workspace.argtypes = [i64, i64, i64, i64, ctypes.POINTER(ctypes.c_size_t)]
         lib.fp8_lora_backward_workspace.restype = ci
+        lib.fp8_nvfp4_quantize.argtypes = [vp, i64, i64, i64, vp, ci, vp, vp, vp, vp, vp]
+        lib.fp8_nvfp4_quantize.restype = ci
+        lib.fp8_nvfp4_dequantize.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp]
+        lib.fp8_nvfp4_dequantize.restype = ci
         lib.fp8_status_string.argtypes = [ci]
         lib.fp8_status_string.restype = ctypes.c_char_p
         lib.fp8_abi_version.argtypes = []
@@ -229,6 +235,29 @@ def fp8_lora_backward(dy, x, lora_b, lora_a, workspace, d_lora_b, d_lora_a, stre
     _check(st, "fp8_lora_backward")
 
 
+def fp8_nvfp4_quantize(x, rows_per_tensor, q, block_scale, global_scale, tensor_amax, xdq=None, amax_given=False,
+                       stream=None):
+    """x bf16 [rows, cols] (rows_per_tensor rows per stacked tensor); q uint8
+    [rows, cols/2]; block_scale uint8 / float8_e4m3fn [rows, cols/16];
+    global_scale, tensor_amax float32 [rows/rows_per_tensor] (tensor_amax is
+    read instead of written when amax_given); xdq optional bf16 [rows, cols]."""
+    _contig(x, q, block_scale, global_scale, tensor_amax, xdq)
+    rows, cols = x.shape
+    st = library().fp8_nvfp4_quantize(_ptr(x), rows, cols, rows_per_tensor, _ptr(tensor_amax), 1 if amax_given else 0,
+                                      _ptr(q), _ptr(block_scale), _ptr(global_scale), _ptr(xdq), _stream(stream, x))
+    _check(st, "fp8_nvfp4_quantize")
+
+
+def fp8_nvfp4_dequantize(q, block_scale, global_scale, rows_per_tensor, x, stream=None):
+    """q uint8 [rows, cols/2], block_scale [rows, cols/16], global_scale
+    float32 [tensors]; x bf16 [rows, cols] output."""
+    _contig(q, block_scale, global_scale, x)
+    rows, cols = x.shape
+    st = library().fp8_nvfp4_dequantize(_ptr(q), _ptr(block_scale), _ptr(global_scale), rows, cols, rows_per_tensor,
+                                        _ptr(x), _stream(stream, q))
+    _check(st, "fp8_nvfp4_dequantize")
+
+
 # --------------------------------------------- allocating conveniences (torch)
 
 def scale_shape(rows, cols, kind):
@@ -296,6 +325,34 @@ def lora_backward(dy, x, lora_b, lora_a, out_dtype=torch.bfloat16, workspace=Non
     return db, da
 
 
+def nvfp4_quantize(x, rows_per_tensor=None, dequant=False, amax=None, stream=None):
+    """Allocate outputs and run fp8_nvfp4_quantize: returns (q uint8
+    [rows, cols/2], block_scale float8_e4m3fn [rows, cols/16], global_scale
+    float32 [T], tensor_amax float32 [T][, xdq]).  ``amax`` (float32 [T] on the
+    device) replaces the measured tensor amax."""
+    rows, cols = x.shape
+    rpt = rows if rows_per_tensor is None else rows_per_tensor
+    t = rows // max(rpt, 1)
+    q = torch.empty((rows, cols // 2), dtype=torch.uint8, device=x.device)
+    bs = torch.empty((rows, cols // 16), dtype=torch.uint8, device=x.device)
+    gs = torch.empty((t,), dtype=torch.float32, device=x.device)
+    am = amax.to(torch.float32).contiguous() if amax is not None else torch.empty((t,), dtype=torch.float32,
+                                                                                  device=x.device)
+    xdq = torch.empty_like(x) if dequant else None
+    fp8_nvfp4_quantize(x, max(rpt, 1), q, bs, gs, am, xdq, amax_given=amax is not None, stream=stream)
+    bs = bs.view(torch.float8_e4m3fn)
+    return (q, bs, gs, am, xdq) if dequant else (q, bs, gs, am)
+
+
+def nvfp4_dequantize(q, block_scale, global_scale, rows_per_tensor=None, stream=None):
+    """Allocate the bf16 output and run fp8_nvfp4_dequantize."""
+    rows = q.shape[0]
+    x = torch.empty((rows, q.shape[1] * 2), dtype=torch.bfloat16, device=q.device)
+    bs = block_scale.view(torch.uint8) if block_scale.dtype != torch.uint8 else block_scale
+    fp8_nvfp4_dequantize(q, bs, global_scale, rows if rows_per_tensor is None else rows_per_tensor, x, stream)
+    return x
+
+
 def dequantize(q, scale, block, stream=None):
     """Allocate the bf16 output and run fp8_block_dequantize."""
     x = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
@@ -303,7 +360,7 @@ def dequantize(q, scale, block, stream=None):
     return x
 
 
-# ------------------------------------------- MXFP8 prequantization of experts
+# ------------------------------------ MXFP8 / NVFP4 prequantization of experts
 
 # Routed MoE expert projections, prefix-tolerant ("fireworks-prequant 0.1.0",
 # "Formats": model.layers.*.mlp.experts.*.{gate,up,down}_proj.weight); dense,
@@ -316,18 +373,24 @@ def is_routed_expert_weight(name):
 
 
 def quantize_state_dict(state, fmt="mxfp8", device="cuda", rule="ceil", out_device=None):
-    """Prequantize the routed expert weights of a state dict to MXFP8.
+    """Prequantize the routed expert weights of a state dict to MXFP8 or NVFP4.
 
     Every tensor whose name is a routed expert projection weight (bf16,
-    [rows, cols] with cols % 32 == 0) is quantized on ``device`` by
-    fp8_block_quantize with 1x32 blocks and E8M0 scales: ``{..}.weight``
-    becomes the float8_e4m3fn codes and ``{..}.weight_scale_inv`` the uint8
-    E8M0 scale codes [rows, cols/32] ("fireworks-prequant 0.1.0", "Quick
-    start").  Other tensors pass through unchanged (the same objects).
-    Quantized outputs stay on ``device`` unless ``out_device`` is given.
+    [rows, cols]) is quantized on ``device`` ("fireworks-prequant 0.1.0",
+    "Quick start", "Formats"):
+      * fmt="mxfp8" (cols % 32 == 0): fp8_block_quantize with 1x32 blocks and
+        E8M0 scales; ``{..}.weight`` becomes the float8_e4m3fn codes and
+        ``{..}.weight_scale_inv`` the uint8 E8M0 scale codes [rows, cols/32];
+      * fmt="nvfp4" (cols % 16 == 0): fp8_nvfp4_quantize, one tensor;
+        ``{..}.weight`` becomes the packed E2M1 codes (uint8 [rows, cols/2]),
+        ``{..}.weight_scale_inv`` the float8_e4m3fn 1x16 block scales
+        [rows, cols/16] and ``{..}.weight_global_scale`` the float32 tensor
+        scale g (shape [1]).
+    Other tensors pass through unchanged (the same objects).  Quantized
+    outputs stay on ``device`` unless ``out_device`` is given.
     """
-    if fmt != "mxfp8":
-        raise ValueError(f"unsupported prequant format {fmt!r} (only 'mxfp8')")
+    if fmt not in ("mxfp8", "nvfp4"):
+        raise ValueError(f"unsupported prequant format {fmt!r} (only 'mxfp8' and 'nvfp4')")
     out = {}
     for name, t in state.items():
         if not is_routed_expert_weight(name):
@@ -336,9 +399,17 @@ def quantize_state_dict(state, fmt="mxfp8", device="cuda", rule="ceil", out_devi
         if t.dtype != torch.bfloat16 or t.dim() != 2:
             raise ValueError(f"{name}: expected a 2-D bf16 tensor, got {t.dtype} {tuple(t.shape)}")
         x = t.to(device).contiguous()
-        q, s = quantize(x, "1x32", rule)
+        stem = name[: -len("weight")]
+        if fmt == "mxfp8":
+            q, s = quantize(x, "1x32", rule)
+            extra = {}
+        else:
+            q, s, g, _ = nvfp4_quantize(x)
+            extra = {stem + "weight_global_scale": g}
         if out_device is not None:
             q, s = q.to(out_device), s.to(out_device)
+            extra = {k: v.to(out_device) for k, v in extra.items()}
         out[name] = q
-        out[name[: -len("weight")] + "weight_scale_inv"] = s
+        out[stem + "weight_scale_inv"] = s
+        out.update(extra)
     return out

@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "libfp8blk.so")
 
-SOURCES = ["quantize.hip", "dequant.hip", "merge.hip", "gemm.hip", "lora_bwd.hip", "abi.cpp"]
+SOURCES = ["quantize.hip", "dequant.hip", "merge.hip", "gemm.hip", "lora_bwd.hip", "nvfp4.hip", "abi.cpp"]
 
 # -ffp-contract=off: every fused multiply-add in the kernels is written out
 # explicitly, so rounding follows the source exactly.  Packed fp32 vector

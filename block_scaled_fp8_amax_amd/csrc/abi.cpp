@@ -221,4 +221,40 @@ int fp8_lora_backward(const uint16_t* dy, const uint16_t* x, const uint16_t* lor
                                             reinterpret_cast<hipStream_t>(stream)));
 }
 
+static int nvfp4_shape(int64_t rows, int64_t cols, int64_t rows_per_tensor) {
+  if (rows < 0 || cols < 0 || cols % 16) return FP8_ERR_SHAPE;
+  if (rows_per_tensor < 1 || rows % rows_per_tensor) return FP8_ERR_SHAPE;
+  if (rows * (cols / 8) > 0xFFF00000ll) return FP8_ERR_SHAPE;  // 32-bit chunk indices, with launch margin
+  return FP8_OK;
+}
+
+int fp8_nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t rows_per_tensor, float* tensor_amax,
+                       int amax_given, uint8_t* q, uint8_t* block_scale, float* global_scale, uint16_t* xdq,
+                       void* stream) {
+  if (amax_given != 0 && amax_given != 1) return FP8_ERR_INVALID_ARG;
+  if (int s = nvfp4_shape(rows, cols, rows_per_tensor)) return s;
+  if (rows == 0 || cols == 0) return FP8_OK;
+  if (!x || !tensor_amax || !q || !block_scale || !global_scale) return FP8_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(q, 8) || !aligned(tensor_amax, 4) || !aligned(global_scale, 4) ||
+      (xdq && !aligned(xdq, 16)))
+    return FP8_ERR_ALIGN;
+  DeviceInfo* dev = nullptr;
+  if (int s = current_device(&dev)) return s;
+  return hip_status(fp8blk::launch_nvfp4_quant(x, rows, cols, rows_per_tensor, tensor_amax, amax_given == 1, q,
+                                               block_scale, global_scale, xdq,
+                                               reinterpret_cast<hipStream_t>(stream)));
+}
+
+int fp8_nvfp4_dequantize(const uint8_t* q, const uint8_t* block_scale, const float* global_scale, int64_t rows,
+                         int64_t cols, int64_t rows_per_tensor, uint16_t* x, void* stream) {
+  if (int s = nvfp4_shape(rows, cols, rows_per_tensor)) return s;
+  if (rows == 0 || cols == 0) return FP8_OK;
+  if (!q || !block_scale || !global_scale || !x) return FP8_ERR_INVALID_ARG;
+  if (!aligned(q, 4) || !aligned(global_scale, 4) || !aligned(x, 16)) return FP8_ERR_ALIGN;
+  DeviceInfo* dev = nullptr;
+  if (int s = current_device(&dev)) return s;
+  return hip_status(fp8blk::launch_nvfp4_dequant(q, block_scale, global_scale, rows, cols, rows_per_tensor, x,
+                                                 reinterpret_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -27,4 +27,10 @@ hipError_t launch_lora_bwd(const uint16_t* dy, const uint16_t* x, const uint16_t
                            int64_t n, int64_t k, int64_t r, void* workspace, void* d_b, void* d_a, bool out_f32,
                            int num_cu, hipStream_t stream);
 
+hipError_t launch_nvfp4_quant(const uint16_t* x, int64_t rows, int64_t cols, int64_t rpt, float* amax,
+                              bool amax_given, uint8_t* q, uint8_t* bs, float* gs, uint16_t* xdq,
+                              hipStream_t stream);
+hipError_t launch_nvfp4_dequant(const uint8_t* q, const uint8_t* bs, const float* gs, int64_t rows, int64_t cols,
+                                int64_t rpt, uint16_t* x, hipStream_t stream);
+
 }  // namespace fp8blk

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define FP8BLK_ABI_VERSION 3
+#define FP8BLK_ABI_VERSION 4
 
 typedef enum {
   FP8_OK = 0,
@@ -266,6 +266,47 @@ int fp8_lora_backward(const uint16_t* dy, const uint16_t* x, const uint16_t* lor
 /* Workspace bytes fp8_lora_backward needs for (m, n, k, r), into *bytes
  * (host pointer).  Same shape checks and status codes as the call itself. */
 int fp8_lora_backward_workspace(int64_t m, int64_t n, int64_t k, int64_t r, size_t* bytes);
+
+/*
+ * fp8_nvfp4_quantize -- NVFP4 prequantization: packed FP4 values with FP8
+ * block scales.
+ *
+ * Defined by: [prequant] "Formats" (nvfp4: packed FP4 + FP8 block scales,
+ * served at FP4) and the routed-expert rule below it.  The page gives no
+ * layout; this library takes E2M1 elements (OCP Microscaling), 1x16 blocks
+ * with e4m3fn scales, and an fp32 scale per tensor:
+ *   A = max |x| over the tensor (or the caller's value), g = RN32(A / 2688)
+ *   S = e4m3(RN32(a / RN32(6 g))), a = the block's amax (RNE, saturating;
+ *       S = 0 when g = 0)
+ *   m = RN32(e4m3(S) * g), code = e2m1(RN32(x / m)) (RNE, saturating at 6,
+ *       sign kept; only the sign when m = 0)
+ *   xdq = RN_bf16(RN32(e2m1(code) * m)).
+ *
+ * x      [rows x cols] bf16 (16-byte aligned); the rows form rows/rows_per_tensor
+ *        stacked tensors of rows_per_tensor rows, each with its own A and g;
+ * tensor_amax [tensors] float: written with A when amax_given == 0, read as
+ *        A (finite, >= 0) when amax_given == 1 (4-byte aligned);
+ * q      [rows x cols/2] bytes out, element 2j in the low nibble of byte j
+ *        (8-byte aligned);
+ * block_scale [rows x cols/16] e4m3fn codes out;
+ * global_scale [tensors] float g out (4-byte aligned);
+ * xdq    optional [rows x cols] bf16 fake-quant output (16-byte aligned).
+ * Shape: cols % 16 == 0, rows % rows_per_tensor == 0, rows * cols / 8 <=
+ *        2^32 - 2^20.  rows == 0 or cols == 0 enqueues nothing.
+ */
+int fp8_nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t rows_per_tensor,
+                       float* tensor_amax, int amax_given, uint8_t* q, uint8_t* block_scale,
+                       float* global_scale, uint16_t* xdq, void* stream);
+
+/*
+ * fp8_nvfp4_dequantize -- NVFP4 codes + scales -> bf16:
+ *   x = RN_bf16(RN32(e2m1(code) * RN32(e4m3(S) * g))), the value
+ * fp8_nvfp4_quantize writes to xdq.  Defined by: [prequant] "Formats"
+ * (serving loads the packed weights); arguments and shape as there (q
+ * 4-byte aligned here).
+ */
+int fp8_nvfp4_dequantize(const uint8_t* q, const uint8_t* block_scale, const float* global_scale,
+                         int64_t rows, int64_t cols, int64_t rows_per_tensor, uint16_t* x, void* stream);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char* fp8_status_string(int status);

@@ -38,6 +38,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == {"fp8_block_quantize", "fp8_block_dequantize", "fp8_fake_quant_merge",
                           "fp8_block_scaled_gemm", "fp8_grouped_gemm", "fp8_grouped_gemm_gather",
                           "fp8_lora_backward", "fp8_lora_backward_workspace",
+                          "fp8_nvfp4_quantize", "fp8_nvfp4_dequantize",
                           "fp8_status_string", "fp8_abi_version"}
     raw = ctypes.CDLL(fb.library_path)
     for n in names:
@@ -45,7 +46,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.fp8_abi_version() == 3
+    assert lib.fp8_abi_version() == 4
     for s in range(6):
         assert len(lib.fp8_status_string(s)) > 0
     assert lib.fp8_status_string(99) == b"unknown status"
@@ -206,4 +207,29 @@ def test_routed_expert_name_rule():
 
 def test_quantize_state_dict_rejects_other_formats():
     with pytest.raises(ValueError):
-        fb.quantize_state_dict({}, fmt="nvfp4")
+        fb.quantize_state_dict({}, fmt="mxfp4")
+    assert fb.quantize_state_dict({"a": 1}, fmt="nvfp4") == {"a": 1}
+
+
+def test_nvfp4_validation(lib):
+    q = lib.fp8_nvfp4_quantize
+    #      x    rows cols rpt amax given q    bs   gs   xdq  stream
+    assert q(A16, 4, 32, 4, A16, 2, A16, A16, A16, None, None) == INVALID     # amax_given not 0/1
+    assert q(A16, 4, 24, 4, A16, 0, A16, A16, A16, None, None) == SHAPE       # cols % 16
+    assert q(A16, 4, 32, 3, A16, 0, A16, A16, A16, None, None) == SHAPE       # rows % rows_per_tensor
+    assert q(A16, 4, 32, 0, A16, 0, A16, A16, A16, None, None) == SHAPE
+    assert q(A16, -4, 32, 4, A16, 0, A16, A16, A16, None, None) == SHAPE
+    assert q(A16, 1 << 22, 1 << 13, 1, A16, 0, A16, A16, A16, None, None) == SHAPE   # >= 2^32 chunks
+    assert q(None, 0, 32, 1, None, 0, None, None, None, None, None) == OK     # empty
+    assert q(None, 4, 32, 4, A16, 0, A16, A16, A16, None, None) == INVALID
+    assert q(A16, 4, 32, 4, None, 0, A16, A16, A16, None, None) == INVALID    # no tensor_amax
+    assert q(A16, 4, 32, 4, A16, 0, A16, None, A16, None, None) == INVALID    # no block scales
+    assert q(A16 + 8, 4, 32, 4, A16, 0, A16, A16, A16, None, None) == ALIGN
+    assert q(A16, 4, 32, 4, A16, 0, A16 + 4, A16, A16, None, None) == ALIGN   # codes: 8 B
+    assert q(A16, 4, 32, 4, A16 + 1, 0, A16, A16, A16, None, None) == ALIGN
+    assert q(A16, 4, 32, 4, A16, 0, A16, A16, A16, A16 + 4, None) == ALIGN    # xdq: 16 B
+    d = lib.fp8_nvfp4_dequantize
+    assert d(A16, A16, A16, 4, 24, 4, A16, None) == SHAPE
+    assert d(None, None, None, 0, 32, 1, None, None) == OK
+    assert d(A16, None, A16, 4, 32, 4, A16, None) == INVALID
+    assert d(A16, A16, A16, 4, 32, 4, A16 + 8, None) == ALIGN
