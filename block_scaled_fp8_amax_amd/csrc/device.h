@@ -159,6 +159,22 @@ __device__ __forceinline__ float e8m0_val(uint32_t code) {
   return code == 0 ? __uint_as_float(0x00400000u) : __uint_as_float(code << 23);
 }
 
+// ------------------------------------------------------------- code stores
+
+// Codes that fit in half the 256 MiB Infinity Cache are written with
+// ordinary stores, so that the GEMM that usually consumes them next finds
+// them cached; larger outputs (a whole layer's prequant) stream past the
+// caches with nontemporal stores.
+constexpr int64_t kCachedCodeBytes = int64_t(128) << 20;
+
+template <bool CACHED, typename T>
+__device__ __forceinline__ void store_code(T v, T* p) {
+  if constexpr (CACHED)
+    *p = v;
+  else
+    __builtin_nontemporal_store(v, p);
+}
+
 // ----------------------------------------------------------- e4m3 packing
 
 // Four fp32 -> four e4m3fn codes in one dword (byte i = value i).

@@ -29,7 +29,7 @@
 
 namespace fp8blk {
 
-template <int RMAX, int CPL, bool DQ>
+template <int RMAX, int CPL, bool DQ, bool CACHED>
 __global__ __launch_bounds__(256) void merge_128_kernel(const uint16_t* __restrict__ w, const uint16_t* __restrict__ lb,
                                                         const uint16_t* __restrict__ la, int64_t k, int r,
                                                         uint8_t* __restrict__ q, float* __restrict__ scale,
@@ -146,7 +146,7 @@ __global__ __launch_bounds__(256) void merge_128_kernel(const uint16_t* __restri
         c[d] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false) & 0xFFFFu;
       }
       if constexpr (DW == 2)
-        __builtin_nontemporal_store(c[0] | (c[1] << 16), reinterpret_cast<uint32_t*>(qb + o));
+        store_code<CACHED>(c[0] | (c[1] << 16), reinterpret_cast<uint32_t*>(qb + o));
       else
         *reinterpret_cast<uint16_t*>(qb + o) = (uint16_t)c[0];
       if constexpr (DQ) {
@@ -174,14 +174,21 @@ hipError_t launch_merge(const uint16_t* w, const uint16_t* lb, const uint16_t* l
                         uint8_t* q, float* scale, uint16_t* wdq, hipStream_t stream) {
   dim3 grid((unsigned)(k / 128), (unsigned)(n / 128));
   const int ri = (int)r;
-#define FP8BLK_MERGE(RM, CP)                                                                                       \
-  do {                                                                                                             \
-    if (wdq)                                                                                                       \
-      hipLaunchKernelGGL((merge_128_kernel<RM, CP, true>), grid, dim3(256), 0, stream, w, lb, la, k, ri, q, scale, \
-                         wdq);                                                                                     \
-    else                                                                                                           \
-      hipLaunchKernelGGL((merge_128_kernel<RM, CP, false>), grid, dim3(256), 0, stream, w, lb, la, k, ri, q,       \
-                         scale, wdq);                                                                              \
+  const bool cached = n * k <= kCachedCodeBytes;
+#define FP8BLK_MERGE(RM, CP)                                                                                         \
+  do {                                                                                                               \
+    if (wdq && cached)                                                                                               \
+      hipLaunchKernelGGL((merge_128_kernel<RM, CP, true, true>), grid, dim3(256), 0, stream, w, lb, la, k, ri, q,    \
+                         scale, wdq);                                                                                \
+    else if (wdq)                                                                                                    \
+      hipLaunchKernelGGL((merge_128_kernel<RM, CP, true, false>), grid, dim3(256), 0, stream, w, lb, la, k, ri, q,   \
+                         scale, wdq);                                                                                \
+    else if (cached)                                                                                                 \
+      hipLaunchKernelGGL((merge_128_kernel<RM, CP, false, true>), grid, dim3(256), 0, stream, w, lb, la, k, ri, q,   \
+                         scale, wdq);                                                                                \
+    else                                                                                                             \
+      hipLaunchKernelGGL((merge_128_kernel<RM, CP, false, false>), grid, dim3(256), 0, stream, w, lb, la, k, ri, q,  \
+                         scale, wdq);                                                                                \
   } while (0)
   if (r <= 16)
     FP8BLK_MERGE(16, 4);

@@ -19,9 +19,12 @@
 //                 whose loads are issued at once (measured faster than a
 //                 capped grid walking the matrix in a grid-stride loop,
 //                 which serializes each wave's loads behind its stores).
-//   quant_128   : 128x128 blocks, one 256-thread workgroup per block; every
-//                 thread keeps its 64 elements in registers between the amax
+//   quant_128   : 128x128 blocks, one 512-thread workgroup per block; every
+//                 thread keeps its 32 elements in registers between the amax
 //                 pass and the encode pass, so the block is read once.
+// Codes go out with ordinary stores when the code matrix fits in half the
+// Infinity Cache (CACHED), with nontemporal stores otherwise; the bf16
+// fake-quant copy is always nontemporal.
 #include "device.h"
 #include "launch.h"
 
@@ -70,7 +73,7 @@ __device__ __forceinline__ u32x2 encode_chunk(const u32x4& v, const F32Block& fb
 }
 
 // BLK = 32 (E8M0 scales) or 128 (fp32 scales).
-template <int BLK, bool FLOOR, bool DQ>
+template <int BLK, bool FLOOR, bool DQ, bool CACHED>
 __global__ __launch_bounds__(kQRowsThreads) void quant_rows_kernel(const u32x4* __restrict__ x, int64_t nchunks,
                                                                    u32x2* __restrict__ q, void* __restrict__ scale,
                                                                    u32x4* __restrict__ xdq) {
@@ -105,7 +108,7 @@ __global__ __launch_bounds__(kQRowsThreads) void quant_rows_kernel(const u32x4* 
       u32x4 dqv;
       const u32x2 c = encode_chunk<F32SCALE, FLOOR, DQ>(v[u], fb, inv, sval, &dqv);
       if (idx < nchunks) {
-        __builtin_nontemporal_store(c, q + idx);
+        store_code<CACHED>(c, q + idx);
         if constexpr (DQ) __builtin_nontemporal_store(dqv, xdq + idx);
         if ((lane & (LANES - 1)) == 0) {
           if constexpr (F32SCALE)
@@ -120,7 +123,7 @@ __global__ __launch_bounds__(kQRowsThreads) void quant_rows_kernel(const u32x4* 
 
 // 128x128 blocks: grid = (cols/128, rows/128), 256 threads.
 // Thread t covers column chunk (t % 16) * 8 of rows (t / 16) + 16 * i.
-template <bool DQ>
+template <bool DQ, bool CACHED>
 __global__ __launch_bounds__(512) void quant_128_kernel(const uint16_t* __restrict__ x, int64_t cols,
                                                         uint8_t* __restrict__ q, float* __restrict__ scale,
                                                         uint16_t* __restrict__ xdq) {
@@ -151,7 +154,7 @@ __global__ __launch_bounds__(512) void quant_128_kernel(const uint16_t* __restri
     u32x4 dqv;
     const u32x2 c = encode_chunk<true, false, DQ>(v[i], fb, 0.f, fb.s, &dqv);
     const int64_t off = (r0 + 32 * i) * cols + c0;
-    __builtin_nontemporal_store(c, reinterpret_cast<u32x2*>(q + off));
+    store_code<CACHED>(c, reinterpret_cast<u32x2*>(q + off));
     if constexpr (DQ) __builtin_nontemporal_store(dqv, reinterpret_cast<u32x4*>(xdq + off));
   }
   if (t == 0) scale[(int64_t)blockIdx.y * (cols / 128) + blockIdx.x] = fb.s;
@@ -169,6 +172,23 @@ static int rows_grid(int64_t nchunks, int num_cu) {
   return (int)need;
 }
 
+template <int BLK, bool FLOOR>
+static void launch_rows(int grid, const u32x4* xv, int64_t nchunks, u32x2* qv, void* scale, u32x4* dv, bool cached,
+                        hipStream_t stream) {
+  if (dv && cached)
+    hipLaunchKernelGGL((quant_rows_kernel<BLK, FLOOR, true, true>), dim3(grid), dim3(kQRowsThreads), 0, stream, xv,
+                       nchunks, qv, scale, dv);
+  else if (dv)
+    hipLaunchKernelGGL((quant_rows_kernel<BLK, FLOOR, true, false>), dim3(grid), dim3(kQRowsThreads), 0, stream, xv,
+                       nchunks, qv, scale, dv);
+  else if (cached)
+    hipLaunchKernelGGL((quant_rows_kernel<BLK, FLOOR, false, true>), dim3(grid), dim3(kQRowsThreads), 0, stream, xv,
+                       nchunks, qv, scale, dv);
+  else
+    hipLaunchKernelGGL((quant_rows_kernel<BLK, FLOOR, false, false>), dim3(grid), dim3(kQRowsThreads), 0, stream, xv,
+                       nchunks, qv, scale, dv);
+}
+
 hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, int blk, bool floor_rule, uint8_t* q,
                              void* scale, uint16_t* xdq, int num_cu, hipStream_t stream) {
   const int64_t nchunks = rows * cols / 8;
@@ -176,38 +196,28 @@ hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, int 
   const u32x4* xv = reinterpret_cast<const u32x4*>(x);
   u32x2* qv = reinterpret_cast<u32x2*>(q);
   u32x4* dv = reinterpret_cast<u32x4*>(xdq);
-  if (blk == 128) {
-    if (xdq)
-      hipLaunchKernelGGL((quant_rows_kernel<128, false, true>), dim3(grid), dim3(kQRowsThreads), 0, stream, xv,
-                         nchunks, qv, scale, dv);
-    else
-      hipLaunchKernelGGL((quant_rows_kernel<128, false, false>), dim3(grid), dim3(kQRowsThreads), 0, stream, xv,
-                         nchunks, qv, scale, dv);
-  } else if (floor_rule) {
-    if (xdq)
-      hipLaunchKernelGGL((quant_rows_kernel<32, true, true>), dim3(grid), dim3(kQRowsThreads), 0, stream, xv,
-                         nchunks, qv, scale, dv);
-    else
-      hipLaunchKernelGGL((quant_rows_kernel<32, true, false>), dim3(grid), dim3(kQRowsThreads), 0, stream, xv,
-                         nchunks, qv, scale, dv);
-  } else {
-    if (xdq)
-      hipLaunchKernelGGL((quant_rows_kernel<32, false, true>), dim3(grid), dim3(kQRowsThreads), 0, stream, xv,
-                         nchunks, qv, scale, dv);
-    else
-      hipLaunchKernelGGL((quant_rows_kernel<32, false, false>), dim3(grid), dim3(kQRowsThreads), 0, stream, xv,
-                         nchunks, qv, scale, dv);
-  }
+  const bool cached = rows * cols <= kCachedCodeBytes;
+  if (blk == 128)
+    launch_rows<128, false>(grid, xv, nchunks, qv, scale, dv, cached, stream);
+  else if (floor_rule)
+    launch_rows<32, true>(grid, xv, nchunks, qv, scale, dv, cached, stream);
+  else
+    launch_rows<32, false>(grid, xv, nchunks, qv, scale, dv, cached, stream);
   return hipGetLastError();
 }
 
 hipError_t launch_quant_128(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* q, float* scale, uint16_t* xdq,
                             hipStream_t stream) {
   dim3 grid((unsigned)(cols / 128), (unsigned)(rows / 128));
-  if (xdq)
-    hipLaunchKernelGGL((quant_128_kernel<true>), grid, dim3(512), 0, stream, x, cols, q, scale, xdq);
+  const bool cached = rows * cols <= kCachedCodeBytes;
+  if (xdq && cached)
+    hipLaunchKernelGGL((quant_128_kernel<true, true>), grid, dim3(512), 0, stream, x, cols, q, scale, xdq);
+  else if (xdq)
+    hipLaunchKernelGGL((quant_128_kernel<true, false>), grid, dim3(512), 0, stream, x, cols, q, scale, xdq);
+  else if (cached)
+    hipLaunchKernelGGL((quant_128_kernel<false, true>), grid, dim3(512), 0, stream, x, cols, q, scale, xdq);
   else
-    hipLaunchKernelGGL((quant_128_kernel<false>), grid, dim3(512), 0, stream, x, cols, q, scale, xdq);
+    hipLaunchKernelGGL((quant_128_kernel<false, false>), grid, dim3(512), 0, stream, x, cols, q, scale, xdq);
   return hipGetLastError();
 }
 
