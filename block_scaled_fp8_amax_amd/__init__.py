@@ -19,7 +19,7 @@ __all__ = [
     "FP8_BLOCK_1x32_E8M0", "FP8_BLOCK_1x128_F32", "FP8_BLOCK_128x128_F32",
     "FP8_E8M0_CEIL", "FP8_E8M0_FLOOR", "FP8_OUT_BF16", "FP8_OUT_F32",
     "Fp8Error", "library", "library_path",
-    "fp8_block_quantize", "fp8_block_dequantize", "fp8_fake_quant_merge", "fp8_block_scaled_gemm",
+    "fp8_block_quantize", "fp8_block_quantize_batch", "fp8_block_dequantize", "fp8_fake_quant_merge", "fp8_block_scaled_gemm",
     "fp8_grouped_gemm", "fp8_grouped_gemm_gather", "fp8_lora_backward", "fp8_lora_backward_workspace",
     "fp8_nvfp4_quantize", "fp8_nvfp4_dequantize",
     "fp8_status_string", "fp8_abi_version",
@@ -32,7 +32,7 @@ FP8_OK = 0
 FP8_BLOCK_1x32_E8M0, FP8_BLOCK_1x128_F32, FP8_BLOCK_128x128_F32 = 0, 1, 2
 FP8_E8M0_CEIL, FP8_E8M0_FLOOR = 0, 1
 FP8_OUT_BF16, FP8_OUT_F32 = 0, 1
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 _KIND_NAMES = {"1x32": FP8_BLOCK_1x32_E8M0, "1x128": FP8_BLOCK_1x128_F32, "128x128": FP8_BLOCK_128x128_F32}
 _RULE_NAMES = {"ceil": FP8_E8M0_CEIL, "floor": FP8_E8M0_FLOOR}
@@ -40,6 +40,13 @@ _RULE_NAMES = {"ceil": FP8_E8M0_CEIL, "floor": FP8_E8M0_FLOOR}
 library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfp8blk.so")
 
 _lib = None
+
+
+class QuantizeJob(ctypes.Structure):
+    """Mirror of fp8_quantize_job (include/fp8blk.h)."""
+    _fields_ = [("x", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("kind", ctypes.c_int), ("rule", ctypes.c_int), ("q", ctypes.c_void_p),
+                ("scale", ctypes.c_void_p), ("xdq", ctypes.c_void_p)]
 
 
 class Fp8Error(RuntimeError):
@@ -58,6 +65,8 @@ def library():
         i64, vp, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
         lib.fp8_block_quantize.argtypes = [vp, i64, i64, ci, ci, vp, vp, vp, vp]
         lib.fp8_block_quantize.restype = ci
+        lib.fp8_block_quantize_batch.argtypes = [ctypes.POINTER(QuantizeJob), ci, vp]
+        lib.fp8_block_quantize_batch.restype = ci
         lib.fp8_block_dequantize.argtypes = [vp, vp, i64, i64, ci, vp, vp]
         lib.fp8_block_dequantize.restype = ci
         lib.fp8_fake_quant_merge.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, vp, vp]
@@ -143,6 +152,22 @@ def fp8_block_quantize(x, kind, rule, q, scale, xdq=None, stream=None):
     st = library().fp8_block_quantize(_ptr(x), rows, cols, _kind(kind), _rule(rule), _ptr(q), _ptr(scale),
                                       _ptr(xdq), _stream(stream, x))
     _check(st, "fp8_block_quantize")
+
+
+def fp8_block_quantize_batch(jobs, stream=None):
+    """jobs: list of (x, kind, rule, q, scale[, xdq]) tuples, each exactly the
+    arguments of fp8_block_quantize; all of them run in one launch."""
+    if not jobs:
+        return
+    arr = (QuantizeJob * len(jobs))()
+    for i, job in enumerate(jobs):
+        x, kind, rule, q, scale = job[:5]
+        xdq = job[5] if len(job) > 5 else None
+        _contig(x, q, scale, xdq)
+        rows, cols = x.shape
+        arr[i] = QuantizeJob(_ptr(x), rows, cols, _kind(kind), _rule(rule), _ptr(q), _ptr(scale), _ptr(xdq))
+    st = library().fp8_block_quantize_batch(arr, len(jobs), _stream(stream, jobs[0][0]))
+    _check(st, "fp8_block_quantize_batch")
 
 
 def fp8_block_dequantize(q, scale, kind, x, stream=None):

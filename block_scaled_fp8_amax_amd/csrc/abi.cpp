@@ -69,8 +69,8 @@ const char* fp8_status_string(int s) {
   }
 }
 
-int fp8_block_quantize(const uint16_t* x, int64_t rows, int64_t cols, int kind, int rule, uint8_t* q, void* scale,
-                       uint16_t* xdq, void* stream) {
+static int quantize_args(const uint16_t* x, int64_t rows, int64_t cols, int kind, int rule, const uint8_t* q,
+                         const void* scale, const uint16_t* xdq) {
   if (!valid_kind(kind)) return FP8_ERR_INVALID_ARG;
   if (kind == FP8_BLOCK_1x32_E8M0 && rule != FP8_E8M0_CEIL && rule != FP8_E8M0_FLOOR) return FP8_ERR_INVALID_ARG;
   if (rows < 0 || cols < 0) return FP8_ERR_SHAPE;
@@ -82,6 +82,35 @@ int fp8_block_quantize(const uint16_t* x, int64_t rows, int64_t cols, int kind, 
   if (!x || !q || !scale) return FP8_ERR_INVALID_ARG;
   if (!aligned(x, 16) || !aligned(q, 16) || (xdq && !aligned(xdq, 16)) || !aligned(scale, scale_align(kind, false)))
     return FP8_ERR_ALIGN;
+  return FP8_OK;
+}
+
+int fp8_block_quantize_batch(const fp8_quantize_job* jobs, int count, void* stream) {
+  if (count < 0 || count > fp8blk::kMaxQuantJobs) return FP8_ERR_INVALID_ARG;
+  if (count == 0) return FP8_OK;
+  if (!jobs) return FP8_ERR_INVALID_ARG;
+  fp8blk::QuantJobIn in[fp8blk::kMaxQuantJobs];
+  int64_t wgs = 0;
+  bool work = false;
+  for (int i = 0; i < count; ++i) {
+    const fp8_quantize_job& j = jobs[i];
+    if (int st = quantize_args(j.x, j.rows, j.cols, j.kind, j.rule, j.q, j.scale, j.xdq)) return st;
+    work = work || (j.rows > 0 && j.cols > 0);
+    if (j.kind != FP8_BLOCK_128x128_F32 && j.rows * (j.cols / 8) > 0xFFF00000ll) return FP8_ERR_SHAPE;
+    wgs += j.kind == FP8_BLOCK_128x128_F32 ? (j.rows / 128) * (j.cols / 128) : j.rows * j.cols / 8 / 2048 + 1;
+    in[i] = fp8blk::QuantJobIn{j.x, j.rows, j.cols, j.kind, j.rule == FP8_E8M0_FLOOR, j.q, j.scale, j.xdq};
+  }
+  if (wgs > 0x7FFFFFFFll) return FP8_ERR_SHAPE;
+  if (!work) return FP8_OK;
+  DeviceInfo* dev = nullptr;
+  if (int st = current_device(&dev)) return st;
+  return hip_status(fp8blk::launch_quant_batch(in, count, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int fp8_block_quantize(const uint16_t* x, int64_t rows, int64_t cols, int kind, int rule, uint8_t* q, void* scale,
+                       uint16_t* xdq, void* stream) {
+  if (int st = quantize_args(x, rows, cols, kind, rule, q, scale, xdq)) return st;
+  if (rows == 0 || cols == 0) return FP8_OK;
   DeviceInfo* dev = nullptr;
   if (int s = current_device(&dev)) return s;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);

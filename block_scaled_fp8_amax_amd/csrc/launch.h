@@ -11,6 +11,30 @@ hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, int 
                              void* scale, uint16_t* xdq, int num_cu, hipStream_t stream);
 hipError_t launch_quant_128(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* q, float* scale, uint16_t* xdq,
                             hipStream_t stream);
+// Batched quantize: jobs already validated (at most kMaxQuantJobs).
+constexpr int kMaxQuantJobs = 16;
+struct QuantJobIn {
+  const uint16_t* x;
+  int64_t rows, cols;
+  int kind;           // 0 = 1x32 E8M0, 1 = 1x128 fp32, 2 = 128x128 fp32
+  bool floor_rule;
+  uint8_t* q;
+  void* scale;
+  uint16_t* xdq;
+};
+struct QuantJob {
+  const uint16_t* x;
+  int64_t rows, cols;
+  uint8_t* q;
+  void* scale;
+  uint16_t* xdq;
+  int kind, floor_rule, cached, blocks_x, wg0, wgs;
+};
+struct QuantBatch {
+  QuantJob job[kMaxQuantJobs];
+  int count;
+};
+hipError_t launch_quant_batch(const QuantJobIn* jobs, int count, hipStream_t stream);
 hipError_t launch_dequant(const uint8_t* q, const void* scale, int64_t rows, int64_t cols, int kind, uint16_t* x,
                           hipStream_t stream);
 hipError_t launch_merge(const uint16_t* w, const uint16_t* lb, const uint16_t* la, int64_t n, int64_t k, int64_t r,

@@ -72,16 +72,14 @@ __device__ __forceinline__ u32x2 encode_chunk(const u32x4& v, const F32Block& fb
   return c;
 }
 
-// BLK = 32 (E8M0 scales) or 128 (fp32 scales).
+// BLK = 32 (E8M0 scales) or 128 (fp32 scales).  Wave `wave` of `nwaves`
+// takes the passes wave, wave + nwaves, ... of 64 * kQRowsU chunks.
 template <int BLK, bool FLOOR, bool DQ, bool CACHED>
-__global__ __launch_bounds__(kQRowsThreads) void quant_rows_kernel(const u32x4* __restrict__ x, int64_t nchunks,
-                                                                   u32x2* __restrict__ q, void* __restrict__ scale,
-                                                                   u32x4* __restrict__ xdq) {
+__device__ __forceinline__ void quant_rows_body(const u32x4* __restrict__ x, int64_t nchunks, u32x2* __restrict__ q,
+                                                void* __restrict__ scale, u32x4* __restrict__ xdq, int64_t wave,
+                                                int64_t nwaves, int lane) {
   constexpr int LANES = BLK / 8;
   constexpr bool F32SCALE = (BLK == 128);
-  const int lane = threadIdx.x & 63;
-  const int64_t wave = (int64_t)blockIdx.x * (kQRowsThreads / 64) + (threadIdx.x >> 6);
-  const int64_t nwaves = (int64_t)gridDim.x * (kQRowsThreads / 64);
   for (int64_t base = wave * 64 * kQRowsU; base < nchunks; base += nwaves * 64 * kQRowsU) {
     u32x4 v[kQRowsU];
 #pragma unroll
@@ -121,16 +119,25 @@ __global__ __launch_bounds__(kQRowsThreads) void quant_rows_kernel(const u32x4* 
   }
 }
 
-// 128x128 blocks: grid = (cols/128, rows/128), 256 threads.
-// Thread t covers column chunk (t % 16) * 8 of rows (t / 16) + 16 * i.
+template <int BLK, bool FLOOR, bool DQ, bool CACHED>
+__global__ __launch_bounds__(kQRowsThreads) void quant_rows_kernel(const u32x4* __restrict__ x, int64_t nchunks,
+                                                                   u32x2* __restrict__ q, void* __restrict__ scale,
+                                                                   u32x4* __restrict__ xdq) {
+  quant_rows_body<BLK, FLOOR, DQ, CACHED>(x, nchunks, q, scale, xdq,
+                                          (int64_t)blockIdx.x * (kQRowsThreads / 64) + (threadIdx.x >> 6),
+                                          (int64_t)gridDim.x * (kQRowsThreads / 64), (int)(threadIdx.x & 63));
+}
+
+// 128x128 block (bx, by) by a 512-thread workgroup: thread t covers column
+// chunk (t % 16) * 8 of rows (t / 16) + 32 * i, i = 0..3; red is 8 words of
+// LDS.
 template <bool DQ, bool CACHED>
-__global__ __launch_bounds__(512) void quant_128_kernel(const uint16_t* __restrict__ x, int64_t cols,
-                                                        uint8_t* __restrict__ q, float* __restrict__ scale,
-                                                        uint16_t* __restrict__ xdq) {
-  __shared__ uint32_t red[8];
+__device__ __forceinline__ void quant_128_body(const uint16_t* __restrict__ x, int64_t cols, uint8_t* __restrict__ q,
+                                               float* __restrict__ scale, uint16_t* __restrict__ xdq, int64_t bx,
+                                               int64_t by, uint32_t* red) {
   const int t = threadIdx.x;
-  const int64_t r0 = (int64_t)blockIdx.y * 128 + (t >> 4);
-  const int64_t c0 = (int64_t)blockIdx.x * 128 + (t & 15) * 8;
+  const int64_t r0 = by * 128 + (t >> 4);
+  const int64_t c0 = bx * 128 + (t & 15) * 8;
   u32x4 v[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -157,7 +164,59 @@ __global__ __launch_bounds__(512) void quant_128_kernel(const uint16_t* __restri
     store_code<CACHED>(c, reinterpret_cast<u32x2*>(q + off));
     if constexpr (DQ) __builtin_nontemporal_store(dqv, reinterpret_cast<u32x4*>(xdq + off));
   }
-  if (t == 0) scale[(int64_t)blockIdx.y * (cols / 128) + blockIdx.x] = fb.s;
+  if (t == 0) scale[by * (cols / 128) + bx] = fb.s;
+}
+
+template <bool DQ, bool CACHED>
+__global__ __launch_bounds__(512) void quant_128_kernel(const uint16_t* __restrict__ x, int64_t cols,
+                                                        uint8_t* __restrict__ q, float* __restrict__ scale,
+                                                        uint16_t* __restrict__ xdq) {
+  __shared__ uint32_t red[8];
+  quant_128_body<DQ, CACHED>(x, cols, q, scale, xdq, blockIdx.x, blockIdx.y, red);
+}
+
+// ------------------------------------------------------------ batched jobs
+
+// Several independent quantizations in one launch of 512-thread
+// workgroups: job j owns workgroups [wg0, wg0 + wgs).  A 128x128 job runs one
+// workgroup per block; a 1x32 / 1x128 job runs the rows body over its
+// workgroups' 8 waves each.  Every job's bytes equal those of its own launch
+// (a block never spans two waves, whatever the grouping into workgroups).
+__global__ __launch_bounds__(512) void quant_batch_kernel(QuantBatch b) {
+  __shared__ uint32_t red[8];
+  int j = 0;
+  while (j + 1 < b.count && (int)blockIdx.x >= b.job[j + 1].wg0) ++j;
+  const QuantJob& J = b.job[j];
+  const int local = (int)blockIdx.x - J.wg0;
+  const bool dq = J.xdq != nullptr;
+  if (J.kind == 2) {
+    const int64_t bx = local % J.blocks_x, by = local / J.blocks_x;
+    if (dq && J.cached) quant_128_body<true, true>(J.x, J.cols, J.q, static_cast<float*>(J.scale), J.xdq, bx, by, red);
+    else if (dq) quant_128_body<true, false>(J.x, J.cols, J.q, static_cast<float*>(J.scale), J.xdq, bx, by, red);
+    else if (J.cached) quant_128_body<false, true>(J.x, J.cols, J.q, static_cast<float*>(J.scale), J.xdq, bx, by, red);
+    else quant_128_body<false, false>(J.x, J.cols, J.q, static_cast<float*>(J.scale), J.xdq, bx, by, red);
+    return;
+  }
+  const u32x4* xv = reinterpret_cast<const u32x4*>(J.x);
+  u32x2* qv = reinterpret_cast<u32x2*>(J.q);
+  u32x4* dv = reinterpret_cast<u32x4*>(J.xdq);
+  const int64_t n = J.rows * J.cols / 8;
+  const int64_t wave = (int64_t)local * 8 + (threadIdx.x >> 6), nwaves = (int64_t)J.wgs * 8;
+  const int lane = (int)(threadIdx.x & 63);
+#define FP8BLK_ROWS(B, F)                                                                  \
+  do {                                                                                     \
+    if (dq && J.cached) quant_rows_body<B, F, true, true>(xv, n, qv, J.scale, dv, wave, nwaves, lane);      \
+    else if (dq) quant_rows_body<B, F, true, false>(xv, n, qv, J.scale, dv, wave, nwaves, lane);           \
+    else if (J.cached) quant_rows_body<B, F, false, true>(xv, n, qv, J.scale, dv, wave, nwaves, lane);     \
+    else quant_rows_body<B, F, false, false>(xv, n, qv, J.scale, dv, wave, nwaves, lane);                  \
+  } while (0)
+  if (J.kind == 1)
+    FP8BLK_ROWS(128, false);
+  else if (J.floor_rule)
+    FP8BLK_ROWS(32, true);
+  else
+    FP8BLK_ROWS(32, false);
+#undef FP8BLK_ROWS
 }
 
 // ------------------------------------------------------------------ launchers
@@ -218,6 +277,38 @@ hipError_t launch_quant_128(const uint16_t* x, int64_t rows, int64_t cols, uint8
     hipLaunchKernelGGL((quant_128_kernel<false, true>), grid, dim3(512), 0, stream, x, cols, q, scale, xdq);
   else
     hipLaunchKernelGGL((quant_128_kernel<false, false>), grid, dim3(512), 0, stream, x, cols, q, scale, xdq);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_batch(const QuantJobIn* jobs, int count, hipStream_t stream) {
+  QuantBatch b;
+  int wg = 0, n = 0;
+  for (int i = 0; i < count; ++i) {
+    const QuantJobIn& in = jobs[i];
+    if (in.rows == 0 || in.cols == 0) continue;
+    QuantJob& J = b.job[n++];
+    J.x = in.x;
+    J.rows = in.rows;
+    J.cols = in.cols;
+    J.q = in.q;
+    J.scale = in.scale;
+    J.xdq = in.xdq;
+    J.kind = in.kind;
+    J.floor_rule = in.floor_rule ? 1 : 0;
+    J.cached = in.rows * in.cols <= kCachedCodeBytes ? 1 : 0;
+    J.blocks_x = (int)(in.cols / 128);
+    J.wg0 = wg;
+    if (in.kind == 2) {
+      J.wgs = (int)((in.rows / 128) * (in.cols / 128));
+    } else {
+      const int64_t per_wg = 8 * 64 * kQRowsU;   // chunks of one pass of a workgroup
+      J.wgs = (int)((in.rows * in.cols / 8 + per_wg - 1) / per_wg);
+    }
+    wg += J.wgs;
+  }
+  b.count = n;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(quant_batch_kernel, dim3(wg), dim3(512), 0, stream, b);
   return hipGetLastError();
 }
 

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define FP8BLK_ABI_VERSION 4
+#define FP8BLK_ABI_VERSION 5
 
 typedef enum {
   FP8_OK = 0,
@@ -105,6 +105,37 @@ typedef enum { FP8_OUT_BF16 = 0, FP8_OUT_F32 = 1 } fp8_out;
  */
 int fp8_block_quantize(const uint16_t* x, int64_t rows, int64_t cols, int kind, int rule,
                        uint8_t* q, void* scale, uint16_t* xdq, void* stream);
+
+/*
+ * fp8_block_quantize_batch -- several independent fp8_block_quantize calls
+ * in one launch.
+ *
+ * Defined by: the same passages as fp8_block_quantize (each job is one such
+ * call); a batch serves several tensors at once, for example a weight and
+ * the activations of one projection ([FP8-DSV3-ru] "Как FP8 встроен в
+ * DeepSeek V3": 128x128 weight blocks and 1x128 activation tiles) or a list
+ * of routed expert projections ([prequant] "Formats").
+ *
+ * jobs   host array of `count` job descriptions (1 <= count <= 16; count 0
+ *        enqueues nothing); each job has exactly the arguments, shape rules,
+ *        alignment and outputs of fp8_block_quantize and gives the same
+ *        bytes.  Jobs with zero rows or columns are skipped.  The jobs'
+ *        buffers must not overlap one another.
+ * Errors: the first invalid job's status is returned and nothing is
+ *        launched; count outside [0, 16] is FP8_ERR_INVALID_ARG.
+ */
+typedef struct {
+  const uint16_t* x;    /* [rows x cols] bf16 */
+  int64_t rows;
+  int64_t cols;
+  int kind;             /* fp8_block */
+  int rule;             /* fp8_e8m0_rule (1x32 only) */
+  uint8_t* q;           /* [rows x cols] codes out */
+  void* scale;          /* scales out, as for fp8_block_quantize */
+  uint16_t* xdq;        /* optional fake-quant output, NULL = not written */
+} fp8_quantize_job;
+
+int fp8_block_quantize_batch(const fp8_quantize_job* jobs, int count, void* stream);
 
 /*
  * fp8_block_dequantize -- block-scaled FP8 codes back to bf16.

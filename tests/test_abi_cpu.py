@@ -35,7 +35,8 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared_functions()
-    assert set(names) == {"fp8_block_quantize", "fp8_block_dequantize", "fp8_fake_quant_merge",
+    assert set(names) == {"fp8_block_quantize", "fp8_block_quantize_batch", "fp8_block_dequantize",
+                          "fp8_fake_quant_merge",
                           "fp8_block_scaled_gemm", "fp8_grouped_gemm", "fp8_grouped_gemm_gather",
                           "fp8_lora_backward", "fp8_lora_backward_workspace",
                           "fp8_nvfp4_quantize", "fp8_nvfp4_dequantize",
@@ -46,7 +47,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.fp8_abi_version() == 4
+    assert lib.fp8_abi_version() == 5
     for s in range(6):
         assert len(lib.fp8_status_string(s)) > 0
     assert lib.fp8_status_string(99) == b"unknown status"
@@ -66,6 +67,29 @@ def test_quantize_validation(lib):
     assert q(A16 + 8, 4, 128, 1, 0, A16, A16, None, None) == ALIGN        # x not 16-B aligned
     assert q(A16, 4, 128, 1, 0, A16, A16 + 2, None, None) == ALIGN        # fp32 scale not 4-B aligned
     assert q(A16, 4, 128, 1, 0, A16, A16, A16 + 4, None) == ALIGN         # xdq not 16-B aligned
+
+
+def test_quantize_batch_validation(lib):
+    Job = fb.QuantizeJob
+    b = lib.fp8_block_quantize_batch
+
+    def arr(*jobs):
+        a = (Job * max(1, len(jobs)))()
+        for i, j in enumerate(jobs):
+            a[i] = j
+        return a
+
+    good = Job(A16, 4, 128, 1, 0, A16, A16, None)
+    assert ctypes.sizeof(Job) == 56
+    assert b(None, 0, None) == OK                                            # nothing to do
+    assert b(arr(), -1, None) == INVALID
+    assert b(arr(*([good] * 17)), 17, None) == INVALID                       # more than 16 jobs
+    assert b(None, 1, None) == INVALID
+    assert b(arr(good, Job(A16, 4, 48, 0, 0, A16, A16, None)), 2, None) == SHAPE     # second job: 48 % 32
+    assert b(arr(Job(A16, 4, 128, 7, 0, A16, A16, None), good), 2, None) == INVALID  # unknown kind
+    assert b(arr(good, Job(A16, 64, 128, 2, 0, A16, A16, None)), 2, None) == SHAPE   # 128x128 rows % 128
+    assert b(arr(good, Job(A16 + 8, 4, 128, 1, 0, A16, A16, None)), 2, None) == ALIGN
+    assert b(arr(Job(None, 0, 128, 1, 0, None, None, None)), 1, None) == OK          # empty job only
 
 
 def test_dequantize_validation(lib):

@@ -16,8 +16,9 @@ import torch
 import block_scaled_fp8_amax_amd as fb
 
 from oracle import codec, quant
-from tests.gpu_helpers import assert_bytes_equal, bf16_from_bits, run_quantize
-from workloads import bf16_bits, dense_projection, expert_factors, expert_weights, mx_small, qat_forward
+from tests.gpu_helpers import assert_bytes_equal, bf16_from_bits, run_quantize, to_np_scale, to_np_u8
+from workloads import (bf16_bits, dense_projection, expert_factors, expert_weights, mx_small, normal_bf16,
+                       qat_forward)
 
 pytestmark = pytest.mark.gpu
 
@@ -225,3 +226,61 @@ def test_determinism_and_geometry():
         parts = [run_quantize(x[i:i + 1024].contiguous(), kind, rule) for i in range(0, 4096, 1024)]
         assert np.array_equal(np.concatenate([p[0] for p in parts]), a[0])
         assert np.array_equal(np.concatenate([p[2] for p in parts]), a[2])
+
+
+def _alloc_outputs(x, kind):
+    rows, cols = x.shape
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    shp, dt = fb.scale_shape(rows, cols, kind)
+    s = torch.full(shp, 0, dtype=dt, device=x.device)
+    return q, s
+
+
+def test_batch_mixed_jobs():
+    """One fp8_block_quantize_batch launch over jobs of every kind and rule,
+    with and without the fake-quant copy, ragged row counts and an empty
+    job: every output byte-identical to the oracle and to its own call."""
+    specs = [((96, 512), "1x32", "ceil", True), ((33, 256), "1x32", "floor", False), ((0, 128), "1x128", "ceil", False),
+             ((257, 1024), "1x128", "ceil", True), ((256, 384), "128x128", "ceil", True),
+             ((128, 7168), "128x128", "ceil", False), ((5, 7168), "1x128", "ceil", False)]
+    jobs, singles = [], []
+    for i, (shape, kind, rule, dq) in enumerate(specs):
+        x = normal_bf16(shape, 1.0, 90 + i, "cuda", 0.01, 50.0, outlier_channels=True)
+        q, s = _alloc_outputs(x, kind)
+        xdq = torch.empty_like(x) if dq else None
+        jobs.append((x, kind, rule, q, s, xdq))
+        singles.append(run_quantize(x, kind, rule, dequant=dq) if shape[0] else None)
+    print("[quantize] batch of", len(jobs), "jobs", flush=True)
+    fb.fp8_block_quantize_batch(jobs)
+    torch.cuda.synchronize()
+    for (x, kind, rule, q, s, xdq), one in zip(jobs, singles):
+        if x.shape[0] == 0:
+            continue
+        oq, os_, odq = quant.quantize(bf16_bits(x), kind, rule)
+        assert_bytes_equal(to_np_u8(q), oq, f"batch {kind} {tuple(x.shape)} codes")
+        assert_bytes_equal(to_np_scale(s), os_, f"batch {kind} scales")
+        assert_bytes_equal(to_np_u8(q), one[0], "batch vs single codes")
+        if xdq is not None:
+            assert_bytes_equal(bf16_bits(xdq), odq, f"batch {kind} fake-quant")
+
+
+def test_batch_dense_projection_pair_and_experts():
+    """The dense projection's W (128x128) and X (1x128) in one launch, and 16
+    routed expert projections (1x32) in one launch: identical bytes to one
+    call per tensor."""
+    d = dense_projection("cuda")
+    fac = expert_factors()
+    tensors = [(d["w"], "128x128"), (d["x"], "1x128")]
+    print("[quantize] batch: dense pair", flush=True)
+    for group in (tensors, [(expert_weights(e, "cuda", fac)[e % 3], "1x32") for e in range(16)]):
+        jobs, ref = [], []
+        for x, kind in group:
+            q, s = _alloc_outputs(x, kind)
+            jobs.append((x, kind, "ceil", q, s))
+            q1, s1 = _alloc_outputs(x, kind)
+            fb.fp8_block_quantize(x, kind, "ceil", q1, s1)
+            ref.append((q1, s1))
+        fb.fp8_block_quantize_batch(jobs)
+        torch.cuda.synchronize()
+        for (x, kind, _, q, s), (q1, s1) in zip(jobs, ref):
+            assert torch.equal(q, q1) and torch.equal(s.view(torch.uint8), s1.view(torch.uint8)), (kind, x.shape)
