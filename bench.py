@@ -14,8 +14,8 @@ Prints one JSON line.  ``value`` is the step's throughput in GEMM TFLOP/s
 (2*M*N*K per step over the measured step time).  ``roofline`` describes the
 dominant kernel (the GEMM): its average duration comes from HIP events on
 the stream the kernel runs on, around a back-to-back loop of it run right
-after the timed region (per-launch events inside the timed region are
-reported beside it).  ``components`` gives every kernel's own time, GB/s and
+after the timed region (its time between per-launch events inside whole
+steps, from the untimed pass below, is reported beside it).  ``components`` gives every kernel's own time, GB/s and
 roofline fraction from a separate, untimed pass with events around each
 launch.
 
@@ -677,12 +677,10 @@ def run(args):
     host_ms = (time.perf_counter() - h0) * 1e3 / max(1, args.warmup)
     torch.cuda.synchronize()
 
-    # timed region: K whole steps; events only around the dominant kernel.
-    # A spin kernel queued first keeps the GPU busy while the host enqueues
-    # the steps, so the GPU-side timestamps see back-to-back device work and
-    # not the host's launch overhead.
-    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-             for _ in range(args.steps)]
+    # timed region: K whole steps between one event pair, nothing else on
+    # the stream.  A spin kernel queued first keeps the GPU busy while the
+    # host enqueues the steps, so the GPU-side timestamps see back-to-back
+    # device work and not the host's launch overhead.
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -690,16 +688,10 @@ def run(args):
     t_start.record()
     for i in range(args.steps):
         for name, fn in wl.launches(args.warmup + i):
-            if name == wl.dominant:
-                pairs[i][0].record()
-                fn()
-                pairs[i][1].record()
-            else:
-                fn()
+            fn()
     t_end.record()
     torch.cuda.synchronize()
     ms_per_step = t_start.elapsed_time(t_end) / args.steps
-    dom_in_step_ms = float(np.mean([s.elapsed_time(e) for s, e in pairs]))
 
     # the dominant call alone, back to back on the same stream, between one
     # event pair: its average duration per launch without the per-launch
@@ -748,7 +740,7 @@ def run(args):
     roof["traffic"] = recorded_traffic(args.config)
     roof["kernel"] = wl.dominant
     roof["kernel_us"] = dom_ms * 1e3
-    roof["kernel_us_in_step"] = dom_in_step_ms * 1e3
+    roof["kernel_us_in_step"] = components[wl.dominant]["us"]
     roof["host_enqueue_us_per_step"] = host_ms * 1e3
 
     if wl.unit == "TFLOP/s":
