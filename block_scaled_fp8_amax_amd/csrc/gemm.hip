@@ -19,9 +19,9 @@
 //   kF32xMX  : A 1x128 fp32, B 1x32 E8M0 (grouped experts):
 //              acc += mfma_scale(A, B, 0, 1, 2^Xb) * sa[m][kb]
 //
-// Tiling: a workgroup of 8 waves computes a BM x BN tile (256x128 for the
-// dense GEMM; 128x256 for the grouped GEMM, whose groups are often only a
-// few hundred rows), each wave a 64x64 block of 4x4 MFMA tiles.  K advances
+// Tiling: a workgroup of 8 waves computes a BM x BN tile (128x256, or
+// 256x128 when N is not a multiple of 256), each wave a 64x64 block of 4x4
+// MFMA tiles.  K advances
 // 128 bytes at a time through a 3-deep ring of LDS stages filled by direct
 // global->LDS loads (global_load_lds_dwordx4): every wave-wide load writes
 // 1 KiB of LDS contiguously, 8 tile rows of 128 bytes.  Within a row the
@@ -553,11 +553,12 @@ static void launch_pp(const GemmParams& p, dim3 grid, bool out_f32, hipStream_t 
     hipLaunchKernelGGL((gemm_pp_kernel<MODE, false, GROUPED, BM, BN>), grid, dim3(512), 0, stream, p);
 }
 
-// Dense: 256x128 tiles, 3 stages (148.5 KiB of LDS, one workgroup per CU);
-// a tile moves 48 KiB per K step for 8.4 MFLOP.
+// Dense: 128x256 tiles (256x128 when n is not a multiple of 256), 3 stages
+// (148.5 KiB of LDS, one workgroup per CU); a tile moves 48 KiB per K step
+// for 8.4 MFLOP.  Bands of 4 m-tiles.
 constexpr int kDenseBand = 4;
-// Grouped: 128x256 tiles (m-tiles of 128 rows waste less on small groups),
-// 256x128 when n is not a multiple of 256; bands of 8 m-tiles.
+// Grouped: the same tiles (m-tiles of 128 rows also waste less on small
+// groups); bands of 8 m-tiles.
 constexpr int kGroupBand = 8;
 
 hipError_t launch_gemm(const uint8_t* a, const void* sa, int a_kind, const uint8_t* b, const void* sb, int b_kind,
@@ -565,8 +566,9 @@ hipError_t launch_gemm(const uint8_t* a, const void* sa, int a_kind, const uint8
   GemmParams p{};
   p.a = a; p.sa = sa; p.b = b; p.sb = sb; p.y = y;
   p.m = m; p.n = n; p.k = k;
-  p.tiles_m = (int)((m + 255) / 256);
-  p.tiles_n = (int)(n / 128);
+  const bool wide = n % 256 == 0;
+  p.tiles_m = (int)(wide ? (m + 127) / 128 : (m + 255) / 256);
+  p.tiles_n = (int)(wide ? n / 256 : n / 128);
   p.band = kDenseBand;
   // persistent: at most one workgroup per CU (the kernel's LDS admits one),
   // a multiple of the 8 XCDs
@@ -574,10 +576,13 @@ hipError_t launch_gemm(const uint8_t* a, const void* sa, int a_kind, const uint8
   const int64_t full = num_cu >= 8 ? num_cu / 8 * 8 : 8;
   const int64_t wgs = tiles < full ? (tiles + 7) / 8 * 8 : full;
   dim3 grid((unsigned)wgs);
-  if (a_kind == 1 && b_kind == 2)
-    launch_pp<kF32xF32, false, 256, 128>(p, grid, out_f32, stream);
-  else
-    launch_pp<kMXxMX, false, 256, 128>(p, grid, out_f32, stream);
+  if (a_kind == 1 && b_kind == 2) {
+    if (wide) launch_pp<kF32xF32, false, 128, 256>(p, grid, out_f32, stream);
+    else launch_pp<kF32xF32, false, 256, 128>(p, grid, out_f32, stream);
+  } else {
+    if (wide) launch_pp<kMXxMX, false, 128, 256>(p, grid, out_f32, stream);
+    else launch_pp<kMXxMX, false, 256, 128>(p, grid, out_f32, stream);
+  }
   return hipGetLastError();
 }
 

@@ -59,14 +59,15 @@ def _rand_bf16(shape, sigma, seed):
     return (torch.randn(shape, generator=g, device="cuda") * sigma).to(torch.bfloat16)
 
 
-@pytest.mark.parametrize("m,n,k", [(128, 128, 128), (257, 384, 512), (1, 128, 256), (64, 256, 1024), (300, 512, 384)])
+@pytest.mark.parametrize("m,n,k", [(128, 128, 128), (257, 384, 512), (1, 128, 256), (64, 256, 1024), (300, 512, 384),
+                                   (700, 768, 384)])
 def test_dense_f32_scales_small(m, n, k):
     aq, sa = _q(_rand_bf16((m, k), 1.0, m + k), "1x128")
     bq, sb = _q(_rand_bf16((n, k), 0.02, n + k), "128x128")
     _check_gemm(aq, sa, "1x128", bq, sb, "128x128", label=f"f32 {m}x{n}x{k}")
 
 
-@pytest.mark.parametrize("m,n,k", [(64, 256, 512), (129, 128, 128), (200, 384, 640)])
+@pytest.mark.parametrize("m,n,k", [(64, 256, 512), (129, 128, 128), (200, 384, 640), (300, 512, 256)])
 def test_mx_small(m, n, k):
     aq, sa = _q(_rand_bf16((m, k), 1.0, m), "1x32")
     bq, sb = _q(_rand_bf16((n, k), 1.0, n), "1x32")
