@@ -43,6 +43,14 @@ int current_device(DeviceInfo** out) {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
+// a * b <= lim for non-negative a, b, without overflowing int64.
+bool product_at_most(int64_t a, int64_t b, int64_t lim) { return b == 0 || a <= lim / b; }
+
+// Element counts beyond 2^60 are rejected before any size arithmetic.
+constexpr int64_t kMaxElements = int64_t(1) << 60;
+// GEMM reductions: per-tile A/B offsets are 32-bit (256 rows x K bytes).
+constexpr int64_t kMaxGemmK = int64_t(1) << 24;
+
 int hip_status(hipError_t e) { return e == hipSuccess ? FP8_OK : FP8_ERR_HIP; }
 
 bool valid_kind(int k) { return k == FP8_BLOCK_1x32_E8M0 || k == FP8_BLOCK_1x128_F32 || k == FP8_BLOCK_128x128_F32; }
@@ -73,7 +81,7 @@ static int quantize_args(const uint16_t* x, int64_t rows, int64_t cols, int kind
                          const void* scale, const uint16_t* xdq) {
   if (!valid_kind(kind)) return FP8_ERR_INVALID_ARG;
   if (kind == FP8_BLOCK_1x32_E8M0 && rule != FP8_E8M0_CEIL && rule != FP8_E8M0_FLOOR) return FP8_ERR_INVALID_ARG;
-  if (rows < 0 || cols < 0) return FP8_ERR_SHAPE;
+  if (rows < 0 || cols < 0 || !product_at_most(rows, cols, kMaxElements)) return FP8_ERR_SHAPE;
   const int64_t bc = kind == FP8_BLOCK_1x32_E8M0 ? 32 : 128;
   if (cols % bc) return FP8_ERR_SHAPE;
   if (kind == FP8_BLOCK_128x128_F32 && rows % 128) return FP8_ERR_SHAPE;
@@ -123,7 +131,7 @@ int fp8_block_quantize(const uint16_t* x, int64_t rows, int64_t cols, int kind, 
 int fp8_block_dequantize(const uint8_t* q, const void* scale, int64_t rows, int64_t cols, int kind, uint16_t* x,
                          void* stream) {
   if (!valid_kind(kind)) return FP8_ERR_INVALID_ARG;
-  if (rows < 0 || cols < 0) return FP8_ERR_SHAPE;
+  if (rows < 0 || cols < 0 || !product_at_most(rows, cols, kMaxElements)) return FP8_ERR_SHAPE;
   const int64_t bc = kind == FP8_BLOCK_1x32_E8M0 ? 32 : 128;
   if (cols % bc) return FP8_ERR_SHAPE;
   if (kind == FP8_BLOCK_128x128_F32 && rows % 128) return FP8_ERR_SHAPE;
@@ -158,6 +166,7 @@ int fp8_block_scaled_gemm(const uint8_t* a_q, const void* a_scale, int a_kind, c
   const bool mxpair = a_kind == FP8_BLOCK_1x32_E8M0 && b_kind == FP8_BLOCK_1x32_E8M0;
   if (!f32pair && !mxpair) return FP8_ERR_UNSUPPORTED;
   if (m < 0 || n < 0 || k < 0 || n % 128 || k % 128) return FP8_ERR_SHAPE;
+  if (m > 0x7FFFFFFFll || n > 0x7FFFFFFFll || k > kMaxGemmK) return FP8_ERR_SHAPE;
   if ((m + 255) / 256 * (n / 128) > 0x7FFFFFFF) return FP8_ERR_SHAPE;
   if (m == 0 || n == 0) return FP8_OK;
   if (!y) return FP8_ERR_INVALID_ARG;
@@ -182,6 +191,7 @@ static int grouped_common(const uint8_t* a_q, const void* a_scale, int a_kind, i
     return FP8_ERR_UNSUPPORTED;
   if (groups < 1 || groups > 1024) return FP8_ERR_INVALID_ARG;
   if (total_m < 0 || n < 0 || k <= 0 || n % 128 || k % 128) return FP8_ERR_SHAPE;
+  if (n > 0x7FFFFFFFll || k > kMaxGemmK) return FP8_ERR_SHAPE;
   if (total_m > 0x7FFFFFFF || (total_m / 128 + groups) * (n / 128) > 0x7FFFFF00) return FP8_ERR_SHAPE;
   if (gather && (a_rows < 0 || a_rows * k > 0xFFFFFFFFll)) return FP8_ERR_SHAPE;  // 32-bit row offsets
   if (total_m == 0 || n == 0) return FP8_OK;
@@ -251,7 +261,7 @@ int fp8_lora_backward(const uint16_t* dy, const uint16_t* x, const uint16_t* lor
 }
 
 static int nvfp4_shape(int64_t rows, int64_t cols, int64_t rows_per_tensor) {
-  if (rows < 0 || cols < 0 || cols % 16) return FP8_ERR_SHAPE;
+  if (rows < 0 || cols < 0 || cols % 16 || !product_at_most(rows, cols, kMaxElements)) return FP8_ERR_SHAPE;
   if (rows_per_tensor < 1 || rows % rows_per_tensor) return FP8_ERR_SHAPE;
   if (rows * (cols / 8) > 0xFFF00000ll) return FP8_ERR_SHAPE;  // 32-bit chunk indices, with launch margin
   return FP8_OK;

@@ -100,8 +100,9 @@ typedef enum { FP8_OUT_BF16 = 0, FP8_OUT_F32 = 1 } fp8_out;
  * xdq   optional (NULL = not written) [rows x cols] bf16 fake-quant output
  *       RN_bf16(RN32(decode(q) * scale)), 16-byte aligned.
  * rule  used by FP8_BLOCK_1x32_E8M0 only (ignored otherwise).
- * Shape: rows, cols >= 0; cols % 32 == 0 (1x32) or cols % 128 == 0;
- *        rows % 128 == 0 for 128x128.
+ * Shape: rows, cols >= 0, rows * cols <= 2^60; cols % 32 == 0 (1x32) or
+ *        cols % 128 == 0; rows % 128 == 0 and rows / 128 <= 65535 for
+ *        128x128.
  */
 int fp8_block_quantize(const uint16_t* x, int64_t rows, int64_t cols, int kind, int rule,
                        uint8_t* q, void* scale, uint16_t* xdq, void* stream);
@@ -205,7 +206,8 @@ int fp8_fake_quant_merge(const uint16_t* w, const uint16_t* lora_b, const uint16
  *        instruction and accumulation is continuous in fp32.
  * y      [m x n] out, bf16 (RN_bf16 of the fp32 result) or float, per y_type
  *        (16-byte aligned).
- * Shape: m >= 0 (any), n % 128 == 0, k % 128 == 0.
+ * Shape: 0 <= m < 2^31, n % 128 == 0, k % 128 == 0, 0 < k <= 2^24 (m == 0 or
+ *        n == 0 is a no-op).
  */
 int fp8_block_scaled_gemm(const uint8_t* a_q, const void* a_scale, int a_kind,
                           const uint8_t* b_q, const void* b_scale, int b_kind,
@@ -228,7 +230,8 @@ int fp8_block_scaled_gemm(const uint8_t* a_q, const void* a_scale, int a_kind,
  * group_offsets: DEVICE int32 [groups+1], off[0] = 0, non-decreasing,
  *     off[groups] = total_m (not checked: a violation is undefined);
  * y [total_m x n] out, bf16 or float per y_type (16-byte aligned).
- * Shape: groups >= 1, total_m >= 0, n % 128 == 0, k % 128 == 0.
+ * Shape: 1 <= groups <= 1024, 0 <= total_m < 2^31, n % 128 == 0,
+ *        k % 128 == 0, 0 < k <= 2^24.
  */
 int fp8_grouped_gemm(const uint8_t* a_q, const void* a_scale, int a_kind,
                      const uint8_t* b_q, const void* b_scale, int b_kind,

@@ -67,6 +67,7 @@ def test_quantize_validation(lib):
     assert q(A16 + 8, 4, 128, 1, 0, A16, A16, None, None) == ALIGN        # x not 16-B aligned
     assert q(A16, 4, 128, 1, 0, A16, A16 + 2, None, None) == ALIGN        # fp32 scale not 4-B aligned
     assert q(A16, 4, 128, 1, 0, A16, A16, A16 + 4, None) == ALIGN         # xdq not 16-B aligned
+    assert q(A16, 1 << 40, 1 << 30, 1, 0, A16, A16, None, None) == SHAPE   # element count overflows
 
 
 def test_quantize_batch_validation(lib):
@@ -132,6 +133,8 @@ def test_gemm_validation(lib):
     assert g(A16, A16, 0, A16, A16 + 1, 0, 8, 128, 128, A16, 0, None) == ALIGN    # E8M0 scales: 4 B
     assert g(A16, A16, 1, A16, A16, 2, 8, 128, 128, A16 + 4, 1, None) == ALIGN    # y: 16 B
     assert g(A16, A16, 1, A16, A16, 2, 8, 128, 128, A16 + 2, 0, None) == ALIGN
+    assert g(A16, A16, 1, A16, A16, 2, 8, 128, (1 << 24) + 128, A16, 0, None) == SHAPE   # K beyond 2^24
+    assert g(A16, A16, 1, A16, A16, 2, 1 << 31, 128, 128, A16, 0, None) == SHAPE        # M beyond 2^31 - 1
 
 
 def test_grouped_validation(lib):
@@ -144,6 +147,7 @@ def test_grouped_validation(lib):
     assert g(A16, A16, 1, A16, A16, 0, A16, 4, 0, 128, 128, A16, 0, None) == OK          # no rows
     assert g(A16, A16, 1, A16, A16, 0, None, 4, 8, 128, 128, A16, 0, None) == INVALID
     assert g(A16, A16, 1, A16, A16, 0, A16 + 2, 4, 8, 128, 128, A16, 0, None) == ALIGN
+    assert g(A16, A16, 1, A16, A16, 0, A16, 4, 8, 128, (1 << 24) + 128, A16, 0, None) == SHAPE   # K beyond 2^24
 
 
 def test_grouped_gather_validation(lib):
@@ -244,6 +248,7 @@ def test_nvfp4_validation(lib):
     assert q(A16, 4, 32, 0, A16, 0, A16, A16, A16, None, None) == SHAPE
     assert q(A16, -4, 32, 4, A16, 0, A16, A16, A16, None, None) == SHAPE
     assert q(A16, 1 << 22, 1 << 13, 1, A16, 0, A16, A16, A16, None, None) == SHAPE   # >= 2^32 chunks
+    assert q(A16, 1 << 50, 1 << 20, 1, A16, 0, A16, A16, A16, None, None) == SHAPE   # element count overflows
     assert q(None, 0, 32, 1, None, 0, None, None, None, None, None) == OK     # empty
     assert q(None, 4, 32, 4, A16, 0, A16, A16, A16, None, None) == INVALID
     assert q(A16, 4, 32, 4, None, 0, A16, A16, A16, None, None) == INVALID    # no tensor_amax
