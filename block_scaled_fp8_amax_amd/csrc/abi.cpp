@@ -105,7 +105,8 @@ int fp8_block_quantize_batch(const fp8_quantize_job* jobs, int count, void* stre
     if (int st = quantize_args(j.x, j.rows, j.cols, j.kind, j.rule, j.q, j.scale, j.xdq)) return st;
     work = work || (j.rows > 0 && j.cols > 0);
     if (j.kind != FP8_BLOCK_128x128_F32 && j.rows * (j.cols / 8) > 0xFFF00000ll) return FP8_ERR_SHAPE;
-    wgs += j.kind == FP8_BLOCK_128x128_F32 ? (j.rows / 128) * (j.cols / 128) : j.rows * j.cols / 8 / 2048 + 1;
+    wgs += j.kind == FP8_BLOCK_128x128_F32 ? (j.rows / 128) * (j.cols / 128)
+                                           : j.rows * j.cols / 8 / fp8blk::kQuantBatchRowsChunks + 1;
     in[i] = fp8blk::QuantJobIn{j.x, j.rows, j.cols, j.kind, j.rule == FP8_E8M0_FLOOR, j.q, j.scale, j.xdq};
   }
   if (wgs > 0x7FFFFFFFll) return FP8_ERR_SHAPE;

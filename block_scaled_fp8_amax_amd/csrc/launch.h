@@ -13,6 +13,9 @@ hipError_t launch_quant_128(const uint16_t* x, int64_t rows, int64_t cols, uint8
                             hipStream_t stream);
 // Batched quantize: jobs already validated (at most kMaxQuantJobs).
 constexpr int kMaxQuantJobs = 16;
+// 8-chunk groups a rows-kind (1x32, 1x128) batch workgroup covers in its one
+// pass: 8 waves x 64 lanes x 2 chunks.
+constexpr int64_t kQuantBatchRowsChunks = 1024;
 struct QuantJobIn {
   const uint16_t* x;
   int64_t rows, cols;

@@ -25,8 +25,8 @@
 //     v_cvt_scalef32_pk_fp4_f32 with scale 1 rounds two fp32 values to E2M1
 //     (nearest even, saturating, sign kept) into one byte; the fake-quant
 //     output decodes with v_cvt_scalef32_pk_f32_fp4.
-//   nvfp4_dequant_kernel: 8 codes (4 bytes) per lane to one 16-byte bf16
-//     store.
+//   nvfp4_dequant_kernel: one 1x16 block per lane, its 8 code bytes to two
+//     16-byte bf16 stores (9% faster than 8 codes per lane).
 #include "device.h"
 #include "launch.h"
 
@@ -34,8 +34,10 @@ namespace fp8blk {
 
 namespace {
 
-constexpr int kNvThreads = 256;
-constexpr int kNvU = 4;          // chunks per lane (dequantize)
+constexpr int kNvThreads = 256;     // zero and amax kernels
+constexpr int kNvQThreads = 64;     // encode kernel (one wave: 2% faster than 256 threads)
+constexpr int kNvDThreads = 256;    // dequantize kernel
+constexpr int kNvU = 1;          // 1x16 blocks per lane (dequantize)
 constexpr int kAmU = 8;          // chunks per lane per round (amax)
 constexpr int kAmRounds = 8;     // rounds per amax workgroup
 constexpr float kGlobalDiv = 2688.0f;
@@ -109,28 +111,27 @@ __device__ __forceinline__ float with_sign_of(float q, float x) {
 constexpr int kNvB = 2;   // blocks per lane
 
 template <bool DQ>
-__global__ __launch_bounds__(kNvThreads) void nvfp4_quant_kernel(const u32x4* __restrict__ x, uint32_t nblocks,
-                                                                 uint32_t bpr, uint32_t rpt,
+__global__ __launch_bounds__(kNvQThreads) void nvfp4_quant_kernel(const u32x4* __restrict__ x, uint32_t nblocks,
+                                                                 uint32_t bpt,
                                                                  const float* __restrict__ amax,
                                                                  u32x2* __restrict__ q, uint8_t* __restrict__ bs,
                                                                  float* __restrict__ gs, u32x4* __restrict__ xdq) {
-  const uint32_t first = blockIdx.x * (uint32_t)(kNvThreads * kNvB) + threadIdx.x;
+  const uint32_t first = blockIdx.x * (uint32_t)(kNvQThreads * kNvB) + threadIdx.x;
   u32x4 v[kNvB][2];
 #pragma unroll
   for (int u = 0; u < kNvB; ++u) {
-    const uint32_t bi = first + u * kNvThreads;
+    const uint32_t bi = first + u * kNvQThreads;
 #pragma unroll
     for (int h = 0; h < 2; ++h)
       v[u][h] = bi < nblocks ? __builtin_nontemporal_load(x + 2 * bi + h) : (u32x4){0u, 0u, 0u, 0u};
   }
 #pragma unroll
   for (int u = 0; u < kNvB; ++u) {
-    const uint32_t bi = first + u * kNvThreads;
+    const uint32_t bi = first + u * kNvQThreads;
     if (bi >= nblocks) continue;
     const uint32_t w[8] = {v[u][0].x, v[u][0].y, v[u][0].z, v[u][0].w, v[u][1].x, v[u][1].y, v[u][1].z, v[u][1].w};
     const uint32_t ab = absmax_bits<8>(w);
-    const uint32_t row = bi / bpr;
-    const uint32_t t = row / rpt;
+    const uint32_t t = bi / bpt;
     const float g = amax[t] / kGlobalDiv;
     const float t6 = 6.0f * g;
     const float a = __uint_as_float(ab << 16);
@@ -178,7 +179,7 @@ __global__ __launch_bounds__(kNvThreads) void nvfp4_quant_kernel(const u32x4* __
     c1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c1, qv[14], qv[15], 1.0f, 3);
     __builtin_nontemporal_store((u32x2){c0, c1}, q + bi);
     bs[bi] = (uint8_t)S;
-    if (bi == t * rpt * bpr) gs[t] = g;
+    if (bi == t * bpt) gs[t] = g;
     if constexpr (DQ) {
       __builtin_nontemporal_store(fp4x8_times(c0, m), xdq + 2 * bi);
       __builtin_nontemporal_store(fp4x8_times(c1, m), xdq + 2 * bi + 1);
@@ -186,25 +187,25 @@ __global__ __launch_bounds__(kNvThreads) void nvfp4_quant_kernel(const u32x4* __
   }
 }
 
-__global__ __launch_bounds__(kNvThreads) void nvfp4_dequant_kernel(const uint32_t* __restrict__ q, uint32_t nchunks,
-                                                                   uint32_t cpr, uint32_t rpt,
+__global__ __launch_bounds__(kNvDThreads) void nvfp4_dequant_kernel(const u32x2* __restrict__ q, uint32_t nblocks,
+                                                                   uint32_t bpt,
                                                                    const uint8_t* __restrict__ bs,
                                                                    const float* __restrict__ gs,
                                                                    u32x4* __restrict__ x) {
-  const uint32_t first = blockIdx.x * (uint32_t)(kNvThreads * kNvU) + threadIdx.x;
-  uint32_t c[kNvU];
+  const uint32_t first = blockIdx.x * (uint32_t)(kNvDThreads * kNvU) + threadIdx.x;
+  u32x2 c[kNvU];
 #pragma unroll
   for (int u = 0; u < kNvU; ++u) {
-    const uint32_t idx = first + u * kNvThreads;
-    c[u] = idx < nchunks ? __builtin_nontemporal_load(q + idx) : 0u;
+    const uint32_t bi = first + u * kNvDThreads;
+    c[u] = bi < nblocks ? __builtin_nontemporal_load(q + bi) : (u32x2){0u, 0u};
   }
 #pragma unroll
   for (int u = 0; u < kNvU; ++u) {
-    const uint32_t idx = first + u * kNvThreads;
-    if (idx >= nchunks) continue;
-    const uint32_t t = (idx / cpr) / rpt;
-    const float m = __builtin_amdgcn_cvt_pk_f32_fp8((int)bs[idx >> 1], false)[0] * gs[t];
-    __builtin_nontemporal_store(fp4x8_times(c[u], m), x + idx);
+    const uint32_t bi = first + u * kNvDThreads;
+    if (bi >= nblocks) continue;
+    const float m = __builtin_amdgcn_cvt_pk_f32_fp8((int)bs[bi], false)[0] * gs[bi / bpt];
+    __builtin_nontemporal_store(fp4x8_times(c[u].x, m), x + 2 * bi);
+    __builtin_nontemporal_store(fp4x8_times(c[u].y, m), x + 2 * bi + 1);
   }
 }
 
@@ -226,25 +227,25 @@ hipError_t launch_nvfp4_quant(const uint16_t* x, int64_t rows, int64_t cols, int
     const uint32_t wpt = (cpt + per - 1) / per;
     hipLaunchKernelGGL(nvfp4_amax_kernel, dim3(tensors * wpt), dim3(kNvThreads), 0, stream, xv, cpt, wpt, ab);
   }
-  const uint32_t nblocks = nchunks / 2, bpr = cpr / 2;
-  const uint32_t per_wg = kNvThreads * kNvB;
+  const uint32_t nblocks = nchunks / 2, bpt = (uint32_t)(rpt * (cpr / 2));
+  const uint32_t per_wg = kNvQThreads * kNvB;
   const dim3 grid((nblocks + per_wg - 1) / per_wg);
   u32x2* qv = reinterpret_cast<u32x2*>(q);
   if (xdq)
-    hipLaunchKernelGGL((nvfp4_quant_kernel<true>), grid, dim3(kNvThreads), 0, stream, xv, nblocks, bpr,
-                       (uint32_t)rpt, amax, qv, bs, gs, reinterpret_cast<u32x4*>(xdq));
+    hipLaunchKernelGGL((nvfp4_quant_kernel<true>), grid, dim3(kNvQThreads), 0, stream, xv, nblocks, bpt, amax, qv,
+                       bs, gs, reinterpret_cast<u32x4*>(xdq));
   else
-    hipLaunchKernelGGL((nvfp4_quant_kernel<false>), grid, dim3(kNvThreads), 0, stream, xv, nblocks, bpr,
-                       (uint32_t)rpt, amax, qv, bs, gs, nullptr);
+    hipLaunchKernelGGL((nvfp4_quant_kernel<false>), grid, dim3(kNvQThreads), 0, stream, xv, nblocks, bpt, amax, qv,
+                       bs, gs, nullptr);
   return hipGetLastError();
 }
 
 hipError_t launch_nvfp4_dequant(const uint8_t* q, const uint8_t* bs, const float* gs, int64_t rows, int64_t cols,
                                 int64_t rpt, uint16_t* x, hipStream_t stream) {
-  const uint32_t nchunks = (uint32_t)(rows * cols / 8);
-  const uint32_t per_wg = kNvThreads * kNvU;
-  hipLaunchKernelGGL(nvfp4_dequant_kernel, dim3((nchunks + per_wg - 1) / per_wg), dim3(kNvThreads), 0, stream,
-                     reinterpret_cast<const uint32_t*>(q), nchunks, (uint32_t)(cols / 8), (uint32_t)rpt, bs, gs,
+  const uint32_t nblocks = (uint32_t)(rows * cols / 16);
+  const uint32_t per_wg = kNvDThreads * kNvU;
+  hipLaunchKernelGGL(nvfp4_dequant_kernel, dim3((nblocks + per_wg - 1) / per_wg), dim3(kNvDThreads), 0, stream,
+                     reinterpret_cast<const u32x2*>(q), nblocks, (uint32_t)(rpt * cols / 16), bs, gs,
                      reinterpret_cast<u32x4*>(x));
   return hipGetLastError();
 }
