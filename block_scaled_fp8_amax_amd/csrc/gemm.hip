@@ -187,16 +187,22 @@ __device__ __forceinline__ void grouped_locate(const GemmParams& p, const int* s
   *rows = (int)(left < BM ? left : BM);
 }
 
-template <int BM, int BN, int STAGES>
+// A scales are loaded in chunks of SC K steps (4 bytes per row and step:
+// one fp32 scale, or the four E8M0 scales of the step's 1x32 blocks).
+template <int BM, int BN, int STAGES, int SC>
 struct Layout {
   static constexpr int kA = BM * kBK;           // bytes of A per stage
   static constexpr int kB = BN * kBK;
-  static constexpr int kSA = BM * 4;            // A scales (fp32 or 4 E8M0 bytes) per row
-  static constexpr int kSB = BN * 4;            // B scales per column (E8M0) or per 128-block x 64 copies (fp32)
-  static constexpr int kStage = kA + kB + kSA + kSB;
+  static constexpr int kSB = BN * 4;            // B scales per column (E8M0), or per 128-column block (fp32)
+  static constexpr int kStage = kA + kB + kSB;
+  // after the stages, a ring of 2 A-scale chunks, each laid out as
+  // [block of 64/SC rows][K step][64/SC rows] x 4 bytes
+  static constexpr int kRing = STAGES * kStage;
+  static constexpr int kChunk = BM * SC * 4;
+  static constexpr int kMain = kRing + 2 * kChunk;
   static constexpr int kTileStride = BN + 4;    // fp32 epilogue staging row stride
   static constexpr int kEpi = BM * kTileStride * 4;
-  static constexpr int kBytes = (STAGES * kStage > kEpi ? STAGES * kStage : kEpi);
+  static constexpr int kBytes = (kMain > kEpi ? kMain : kEpi);
 };
 
 // ---------------------------------------------------------------------------
@@ -213,8 +219,10 @@ struct Layout {
 //   half-step 2kb+1 : group 0 compute(kb)  | group 1 memory(kb)
 // The 8-row blocks of the A and B tiles are dealt to the 8 waves in turn,
 // so each memory phase issues half of a stage's loads.  Group 0 also loads
-// the A scales, group 1 the B scales.  A stage is read at half-steps 2kb
-// and 2kb+1 and refilled from half-step 2kb+6 on (3 stages).
+// the A scales, a chunk of several K steps at a time into a ring of two
+// chunks (the chunk starting at step kb is issued first among the loads of
+// stage kb), group 1 the B scales.  A stage is read at half-steps 2kb and
+// 2kb+1 and refilled from half-step 2kb+6 on (3 stages).
 template <int MODE, bool OUT_F32, bool GROUPED, int BM, int BN>
 __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmParams p) {
   constexpr int STAGES = 3, NW = 8;
@@ -223,7 +231,14 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmParams p) {
   static_assert(WMB * GNB == 4, "each group is 4 waves of 64x64");
   constexpr bool A_MX = (MODE == kMXxMX);
   constexpr bool B_MX = (MODE != kF32xF32);
-  using L = Layout<BM, BN, STAGES>;
+  constexpr int SLB = 64 / (BN / 128);         // fp32 B scales: lanes per 128-column block
+  // K steps per A-scale chunk (2 where the grouped kernel's group table
+  // would not fit beside a 4-step ring), rows per A-scale load, and loads
+  // per group-0 wave and chunk
+  constexpr int SC = (GROUPED && BM == 256) ? 2 : 4;
+  constexpr int RPL = 64 / SC;
+  constexpr int LPW = BM / RPL / 4;
+  using L = Layout<BM, BN, STAGES, SC>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[L::kBytes];
   __shared__ int s_grp[GROUPED ? 2 * 1025 : 1];   // grouped: offsets and m-tile prefix
 
@@ -295,31 +310,49 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmParams p) {
       b_off[j] = (uint32_t)(r * K) + (uint32_t)((slot ^ swz(r)) * 16);
     }
   }
-  // Every wave issues exactly one scale load per stage (waves whose block
-  // index repeats reload the same bytes), so that the per-wave load count
-  // is a compile-time constant.  Scale bases are per tile, offsets small.
+  // A scales, loaded by group 0 one chunk of SC K steps at a time: load j
+  // of wave gw covers the RPL-row block j * 4 + gw, lane l reading row
+  // l % RPL of the block at step l / RPL of the chunk.  A load thus touches
+  // RPL rows of the scale array instead of 64, and the rows are what costs
+  // (they are K / 128 or K / 32 bytes apart).  Rows past the end of A
+  // re-read the last valid row, steps past K the last step.
+  const int64_t a_row_bytes = A_MX ? K / 32 : (int64_t)KB * 4;
+  const uint8_t* sa_base = reinterpret_cast<const uint8_t*>(p.sa) + (gather ? 0 : m0 * a_row_bytes);
+  uint32_t c_off[LPW];
+#pragma unroll
+  for (int j = 0; j < LPW; ++j) {
+    const int r = (j * 4 + gw) * RPL + lane % RPL;
+    const int rr = r < mrows ? r : mrows - 1;
+    c_off[j] = (uint32_t)(a_row(rr) * a_row_bytes);
+  }
+  auto issue_chunk = [&](int c) {
+    const uint32_t cbase = lds0 + L::kRing + (c & 1) * L::kChunk;
+    int ks = c * SC + lane / RPL;
+    ks = ks < KB ? ks : KB - 1;
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) dma4(sa_base, c_off[j] + (uint32_t)ks * 4, cbase + (j * 4 + gw) * 256);
+  };
+  // B scales, one load per stage by group 1: a wave issues one only when no
+  // wave before it loads the same scales.  Scale bases are per tile,
+  // offsets small.
   uint32_t s_off = 0, s_lds = 0;
   const uint8_t* s_base = nullptr;
+  bool s_load = false;
   if (grp == 0) {
-    const int rb = gw % WMB;
-    const int r = rb * 64 + lane;
-    const int rr = r < mrows ? r : mrows - 1;
-    const int64_t row_bytes = A_MX ? K / 32 : (int64_t)KB * 4;
-    s_base = reinterpret_cast<const uint8_t*>(p.sa) + (gather ? 0 : m0 * row_bytes);
-    s_off = (uint32_t)(a_row(rr) * row_bytes);
-    s_lds = L::kA + L::kB + rb * 256;
   } else if constexpr (B_MX) {
+    s_load = gw < BN / 64;
     const int cb = gw % (BN / 64);
     s_base = sb8 + n0 * (K / 32);
     s_off = (uint32_t)((cb * 64 + lane) * (K / 32));
-    s_lds = L::kA + L::kB + L::kSA + cb * 256;
+    s_lds = L::kA + L::kB + cb * 256;
   } else {
-    // one fp32 scale per 128-column block and K step, copied by all 64
-    // lanes (a broadcast), so no ordinary vector load is needed in the loop
-    const int j = gw % (BN / 128);
-    s_base = sb8 + ((n0 / 128) + j) * (int64_t)KB * 4;
-    s_off = 0;
-    s_lds = L::kA + L::kB + L::kSA + j * 256;
+    // one fp32 scale per 128-column block and K step: one wave loads every
+    // block's, lane l the scale of block l / SLB, so a block's scale is
+    // read from LDS at a wave-uniform address (a broadcast)
+    s_load = gw == 0;
+    s_base = sb8 + (n0 / 128) * (int64_t)KB * 4;
+    s_off = (uint32_t)((lane / SLB) * KB * 4);
+    s_lds = L::kA + L::kB;
   }
   constexpr int PER = A_PER + B_PER + 1;
   // load i (0 .. PER-1) of this wave's share of stage kb
@@ -330,10 +363,13 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmParams p) {
       dma16(aq, a_off[i] + koff, sbase + (i * NW + wave) * 1024);
     else if (i < A_PER + B_PER)
       dma16(bt, b_off[i - A_PER] + koff, sbase + L::kA + ((i - A_PER) * NW + wave) * 1024);
-    else
+    else if (s_load)
       dma4(s_base, s_off + (uint32_t)kb * 4, sbase + s_lds);
   };
+  // a stage's loads; group 0 issues the A-scale chunk that starts at stage
+  // kb before them, so that the chunk has landed once the stage has
   auto issue = [&](int kb) {
+    if (grp == 0 && kb % SC == 0) issue_chunk(kb / SC);
 #pragma unroll
     for (int i = 0; i < PER; ++i) issue_one(kb, i);
   };
@@ -358,8 +394,12 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmParams p) {
     constexpr bool do_load = decltype(do_load_t)::value;
     const uint8_t* sA = smem + (kb % STAGES) * L::kStage;
     const uint8_t* sB = sA + L::kA;
-    const uint32_t* sSA = reinterpret_cast<const uint32_t*>(sA + L::kA + L::kB);
-    const uint32_t* sSB = sSA + BM;
+    const uint32_t* sSB = reinterpret_cast<const uint32_t*>(sA + L::kA + L::kB);
+    // A scales of row r at step kb: sSC[(r / RPL) * 64 + r % RPL]
+    const uint32_t* sSC = reinterpret_cast<const uint32_t*>(smem + L::kRing + ((kb / SC) & 1) * L::kChunk) + (kb % SC) * RPL;
+    if constexpr (do_load) {
+      if (grp == 0 && (kb + STAGES - 1) % SC == 0) issue_chunk((kb + STAGES - 1) / SC);
+    }
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
       const int ar = wm * 64 + mi * 16 + fr;
@@ -368,9 +408,10 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmParams p) {
       af[mi] = make_frag(*reinterpret_cast<const u32x4*>(rowp + s0), *reinterpret_cast<const u32x4*>(rowp + (s0 ^ 64)));
       if constexpr (do_load) issue_one(kb + STAGES - 1, mi);
       if constexpr (A_MX) {
-        xa[mi] = (int)((sSA[ar] >> (8 * fg)) & 0xFFu);
+        xa[mi] = (int)((sSC[(ar / RPL) * 64 + ar % RPL] >> (8 * fg)) & 0xFFu);
       } else {
-        const u32x4 s4 = *reinterpret_cast<const u32x4*>(&sSA[wm * 64 + mi * 16 + 4 * fg]);
+        const int r0 = wm * 64 + mi * 16 + 4 * fg;   // 4 rows in one block of RPL (>= 16) rows
+        const u32x4 s4 = *reinterpret_cast<const u32x4*>(&sSC[(r0 / RPL) * 64 + r0 % RPL]);
         sc[mi][0] = __uint_as_float(s4.x);
         sc[mi][1] = __uint_as_float(s4.y);
         sc[mi][2] = __uint_as_float(s4.z);
@@ -388,7 +429,7 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmParams p) {
       }
       if constexpr (B_MX) xb[ni] = (int)((sSB[bc] >> (8 * fg)) & 0xFFu);
     }
-    if constexpr (MODE == kF32xF32) sbk = __uint_as_float(sSB[(wn >> 1) * 64]);
+    if constexpr (MODE == kF32xF32) sbk = __uint_as_float(sSB[(wn >> 1) * SLB]);
     if constexpr (do_load) {
 #pragma unroll
       for (int i = 8; i < PER; ++i) issue_one(kb + STAGES - 1, i);
@@ -457,8 +498,10 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmParams p) {
 
   // wait until this wave's share of stage kb has landed (the next stage may
   // stay in flight); then the barrier makes every share visible
-  auto wait_stage = [&](int kb, int per_stage) {
-    if (kb + 1 < KB) wait_vmcnt(per_stage); else wait_vmcnt(0);
+  auto wait_stage = [&](int kb) {
+    if (kb + 1 >= KB) wait_vmcnt(0);
+    else if (s_load) wait_vmcnt(PER);
+    else wait_vmcnt(PER - 1);
   };
   auto half_barrier = [&]() {
     __builtin_amdgcn_sched_barrier(0);
@@ -471,7 +514,7 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmParams p) {
   const int kl = KB > STAGES - 1 ? KB - (STAGES - 1) : 0;
   if (grp == 0) {
     auto step = [&](int kb, auto do_load) {
-      wait_stage(kb, PER);
+      wait_stage(kb);
       half_barrier();              // half-step 2kb: memory
       mem_phase(kb, do_load);
       half_barrier();              // half-step 2kb+1: compute
@@ -481,12 +524,12 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmParams p) {
     for (int kb = kl; kb < KB; ++kb) step(kb, std::false_type{});
     half_barrier();                // half-step 2KB
   } else {
-    wait_stage(0, PER);
+    wait_stage(0);
     half_barrier();                // half-step 0
     auto step = [&](int kb, auto do_load) {
       half_barrier();              // half-step 2kb+1: memory
       mem_phase(kb, do_load);
-      if (kb + 1 < KB) wait_stage(kb + 1, PER);
+      if (kb + 1 < KB) wait_stage(kb + 1);
       half_barrier();              // half-step 2kb+2: compute
       compute_phase();
     };
@@ -554,7 +597,7 @@ static void launch_pp(const GemmParams& p, dim3 grid, bool out_f32, hipStream_t 
 }
 
 // Dense: 128x256 tiles (256x128 when n is not a multiple of 256), 3 stages
-// (148.5 KiB of LDS, one workgroup per CU); a tile moves 48 KiB per K step
+// (151 or 153.5 KiB of LDS with the A-scale ring, one workgroup per CU); a tile moves 48 KiB per K step
 // for 8.4 MFLOP.  Bands of 4 m-tiles.
 constexpr int kDenseBand = 4;
 // Grouped: the same tiles (m-tiles of 128 rows also waste less on small
