@@ -139,14 +139,12 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
 // (memory-bound) groups.  The grid is persistent: one workgroup per CU;
 // workgroup b (XCD b mod 8, slot b / 8) takes slot b / 8 of every window of
 // its XCD in turn.
-// s_off / s_pref: LDS of groups + 1 ints each; returns the tile count.
+// s_pref: LDS of groups + 1 ints; returns the tile count.
 template <int BM>
-__device__ __forceinline__ int grouped_prefix(const GemmParams& p, int* s_off, int* s_pref, int nthreads) {
+__device__ __forceinline__ int grouped_prefix(const GemmParams& p, int* s_pref, int nthreads) {
   const int groups = p.groups;
   const int t = threadIdx.x;
-  for (int g = t; g <= groups; g += nthreads) s_off[g] = p.offsets[g];
-  __syncthreads();
-  for (int g = t; g < groups; g += nthreads) s_pref[g + 1] = (s_off[g + 1] - s_off[g] + BM - 1) / BM;
+  for (int g = t; g < groups; g += nthreads) s_pref[g + 1] = (p.offsets[g + 1] - p.offsets[g] + BM - 1) / BM;
   if (t == 0) s_pref[0] = 0;
   __syncthreads();
   for (int d = 1; d < groups; d <<= 1) {  // inclusive scan of s_pref[1..groups]
@@ -163,7 +161,7 @@ __device__ __forceinline__ int grouped_prefix(const GemmParams& p, int* s_off, i
 
 // Tile L (< the tile count) -> group, first row, rows, n-tile.
 template <int BM>
-__device__ __forceinline__ void grouped_locate(const GemmParams& p, const int* s_off, const int* s_pref, int L,
+__device__ __forceinline__ void grouped_locate(const GemmParams& p, const int* s_pref, int L,
                                                int* g_out, int64_t* row0, int* rows, int* tn_out) {
   const int tiles_n = p.tiles_n;
   const int slot = L / tiles_n;
@@ -182,24 +180,45 @@ __device__ __forceinline__ void grouped_locate(const GemmParams& p, const int* s
   const int tm = b * band + rr % rows_here;
   *g_out = g;
   *tn_out = rr / rows_here;
-  *row0 = (int64_t)s_off[g] + (int64_t)tm * BM;
-  const int64_t left = (int64_t)s_off[g + 1] - *row0;
+  *row0 = (int64_t)p.offsets[g] + (int64_t)tm * BM;
+  const int64_t left = (int64_t)p.offsets[g + 1] - *row0;
   *rows = (int)(left < BM ? left : BM);
 }
 
-// A scales are loaded in chunks of SC K steps (4 bytes per row and step:
-// one fp32 scale, or the four E8M0 scales of the step's 1x32 blocks).
-template <int BM, int BN, int STAGES, int SC>
+// Row scales of A (and column scales of an E8M0-scaled B) are loaded in
+// chunks of several K steps, 4 bytes per row and step: one fp32 scale, or
+// the four E8M0 scales of the step's 1x32 blocks.  A chunk of SC steps is
+// laid out as [block of 64/SC rows][K step][64/SC rows] x 4 bytes, so that
+// one 64-lane load fills one block.
+constexpr int kLdsMax = 160 * 1024;
+constexpr int kGroupTable = 1025 * 4;           // grouped: m-tile prefix of up to 1024 groups
+
+// LDS bytes of a kernel with 3 stages and chunks of sa (A) and sb (B) steps
+constexpr int pp_lds_bytes(int bm, int bn, bool b_mx, bool grouped, int sa, int sb) {
+  return 3 * (bm * 128 + bn * 128 + (b_mx ? 0 : 256)) + 2 * bm * sa * 4 + (b_mx ? 2 * bn * sb * 4 : 0) +
+         (grouped ? kGroupTable : 4);
+}
+// Chunk lengths: 4 K steps where they fit, else 2 (B first)
+template <int BM, int BN, bool B_MX, bool GROUPED>
+struct ChunkSteps {
+  static constexpr int B = pp_lds_bytes(BM, BN, B_MX, GROUPED, 4, 4) <= kLdsMax ? 4 : 2;
+  static constexpr int A = pp_lds_bytes(BM, BN, B_MX, GROUPED, 4, B) <= kLdsMax ? 4 : 2;
+  static_assert(pp_lds_bytes(BM, BN, B_MX, GROUPED, A, B) <= kLdsMax, "LDS");
+};
+
+template <int BM, int BN, int STAGES, bool B_MX, int SCA, int SCB>
 struct Layout {
   static constexpr int kA = BM * kBK;           // bytes of A per stage
   static constexpr int kB = BN * kBK;
-  static constexpr int kSB = BN * 4;            // B scales per column (E8M0), or per 128-column block (fp32)
+  static constexpr int kSB = B_MX ? 0 : 256;    // fp32 B scales: one per 128-column block, in 64/(BN/128) lanes
   static constexpr int kStage = kA + kB + kSB;
-  // after the stages, a ring of 2 A-scale chunks, each laid out as
-  // [block of 64/SC rows][K step][64/SC rows] x 4 bytes
-  static constexpr int kRing = STAGES * kStage;
-  static constexpr int kChunk = BM * SC * 4;
-  static constexpr int kMain = kRing + 2 * kChunk;
+  // after the stages, a ring of 2 A-scale chunks, then (E8M0 B) a ring of
+  // 2 B-scale chunks
+  static constexpr int kRingA = STAGES * kStage;
+  static constexpr int kChunkA = BM * SCA * 4;
+  static constexpr int kRingB = kRingA + 2 * kChunkA;
+  static constexpr int kChunkB = B_MX ? BN * SCB * 4 : 0;
+  static constexpr int kMain = kRingB + 2 * kChunkB;
   static constexpr int kTileStride = BN + 4;    // fp32 epilogue staging row stride
   static constexpr int kEpi = BM * kTileStride * 4;
   static constexpr int kBytes = (kMain > kEpi ? kMain : kEpi);
@@ -220,9 +239,9 @@ struct Layout {
 // The 8-row blocks of the A and B tiles are dealt to the 8 waves in turn,
 // so each memory phase issues half of a stage's loads.  Group 0 also loads
 // the A scales, a chunk of several K steps at a time into a ring of two
-// chunks (the chunk starting at step kb is issued first among the loads of
-// stage kb), group 1 the B scales.  A stage is read at half-steps 2kb and
-// 2kb+1 and refilled from half-step 2kb+6 on (3 stages).
+// chunks (the chunk starting at step kb is issued with the loads of stage
+// kb), group 1 the B scales (E8M0 B in chunks too).  A stage is read at
+// half-steps 2kb and 2kb+1 and refilled from half-step 2kb+6 on (3 stages).
 template <int MODE, bool OUT_F32, bool GROUPED, int BM, int BN>
 __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmParams p) {
   constexpr int STAGES = 3, NW = 8;
@@ -232,15 +251,15 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmParams p) {
   constexpr bool A_MX = (MODE == kMXxMX);
   constexpr bool B_MX = (MODE != kF32xF32);
   constexpr int SLB = 64 / (BN / 128);         // fp32 B scales: lanes per 128-column block
-  // K steps per A-scale chunk (2 where the grouped kernel's group table
-  // would not fit beside a 4-step ring), rows per A-scale load, and loads
-  // per group-0 wave and chunk
-  constexpr int SC = (GROUPED && BM == 256) ? 2 : 4;
-  constexpr int RPL = 64 / SC;
-  constexpr int LPW = BM / RPL / 4;
-  using L = Layout<BM, BN, STAGES, SC>;
+  // K steps per scale chunk; rows (columns) per scale load; loads per
+  // wave and chunk (group 0 loads A's chunks, group 1 B's)
+  constexpr int SCA = ChunkSteps<BM, BN, B_MX, GROUPED>::A;
+  constexpr int SCB = ChunkSteps<BM, BN, B_MX, GROUPED>::B;
+  constexpr int RPLA = 64 / SCA, RPLB = 64 / SCB;
+  constexpr int LPWA = BM / RPLA / 4, LPWB = B_MX ? BN / RPLB / 4 : 1;
+  using L = Layout<BM, BN, STAGES, B_MX, SCA, SCB>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[L::kBytes];
-  __shared__ int s_grp[GROUPED ? 2 * 1025 : 1];   // grouped: offsets and m-tile prefix
+  __shared__ int s_grp[GROUPED ? kGroupTable / 4 : 1];   // grouped: m-tile prefix
 
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -252,7 +271,7 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmParams p) {
   const int64_t K = p.k;
   const int KB = (int)(K / kBK);
   int n_tiles = 1;
-  if constexpr (GROUPED) n_tiles = grouped_prefix<BM>(p, s_grp, s_grp + 1025, NW * 64);
+  if constexpr (GROUPED) n_tiles = grouped_prefix<BM>(p, s_grp, NW * 64);
 
   // this workgroup's tiles in turn (persistent grid)
   for (int it = 0;; ++it) {
@@ -266,7 +285,7 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmParams p) {
     const int tile = (it * 8 + (int)(blockIdx.x & 7)) * wsz + (int)(blockIdx.x >> 3);
     if (tile >= n_tiles) break;
     int g, tn;
-    grouped_locate<BM>(p, s_grp, s_grp + 1025, tile, &g, &m0, &mrows, &tn);
+    grouped_locate<BM>(p, s_grp, tile, &g, &m0, &mrows, &tn);
     g = __builtin_amdgcn_readfirstlane(g);
     tn = __builtin_amdgcn_readfirstlane(tn);
     m0 = (int64_t)__builtin_amdgcn_readfirstlane((int)m0);
@@ -310,41 +329,51 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmParams p) {
       b_off[j] = (uint32_t)(r * K) + (uint32_t)((slot ^ swz(r)) * 16);
     }
   }
-  // A scales, loaded by group 0 one chunk of SC K steps at a time: load j
-  // of wave gw covers the RPL-row block j * 4 + gw, lane l reading row
-  // l % RPL of the block at step l / RPL of the chunk.  A load thus touches
-  // RPL rows of the scale array instead of 64, and the rows are what costs
-  // (they are K / 128 or K / 32 bytes apart).  Rows past the end of A
-  // re-read the last valid row, steps past K the last step.
+  // Scale chunks.  Group 0 loads A's, group 1 (E8M0 B) B's, one chunk of
+  // SC K steps at a time: load j of wave gw covers the block j * 4 + gw of
+  // 64 / SC rows (columns), lane l reading row l % (64 / SC) of the block at
+  // step l / (64 / SC) of the chunk.  A load thus touches 16 or 32 rows of
+  // the scale array instead of 64, and the rows are what costs (they are
+  // K / 128 or K / 32 bytes apart).  Rows past the end of A re-read the last
+  // valid row, steps past K the last step.
+  constexpr int LPW = LPWA > LPWB ? LPWA : LPWB;
   const int64_t a_row_bytes = A_MX ? K / 32 : (int64_t)KB * 4;
-  const uint8_t* sa_base = reinterpret_cast<const uint8_t*>(p.sa) + (gather ? 0 : m0 * a_row_bytes);
+  const uint8_t* c_base;
   uint32_t c_off[LPW];
+  uint32_t c_ring;
+  int c_steps, c_rows, c_loads;
+  if (grp == 0) {
+    c_base = reinterpret_cast<const uint8_t*>(p.sa) + (gather ? 0 : m0 * a_row_bytes);
 #pragma unroll
-  for (int j = 0; j < LPW; ++j) {
-    const int r = (j * 4 + gw) * RPL + lane % RPL;
-    const int rr = r < mrows ? r : mrows - 1;
-    c_off[j] = (uint32_t)(a_row(rr) * a_row_bytes);
+    for (int j = 0; j < LPW; ++j) {
+      const int r = (j * 4 + gw) * RPLA + lane % RPLA;
+      const int rr = r < mrows ? r : mrows - 1;
+      c_off[j] = (uint32_t)(a_row(rr) * a_row_bytes);
+    }
+    c_ring = L::kRingA;
+    c_steps = SCA; c_rows = RPLA; c_loads = LPWA;
+  } else {
+    c_base = sb8 + n0 * (K / 32);
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) c_off[j] = (uint32_t)(((j * 4 + gw) * RPLB + lane % RPLB) * (K / 32));
+    c_ring = L::kRingB;
+    c_steps = SCB; c_rows = RPLB; c_loads = B_MX ? LPWB : 0;
   }
+  const uint32_t c_chunk = grp == 0 ? L::kChunkA : L::kChunkB;
   auto issue_chunk = [&](int c) {
-    const uint32_t cbase = lds0 + L::kRing + (c & 1) * L::kChunk;
-    int ks = c * SC + lane / RPL;
+    const uint32_t cbase = lds0 + c_ring + (c & 1) * c_chunk;
+    int ks = c * c_steps + lane / c_rows;
     ks = ks < KB ? ks : KB - 1;
 #pragma unroll
-    for (int j = 0; j < LPW; ++j) dma4(sa_base, c_off[j] + (uint32_t)ks * 4, cbase + (j * 4 + gw) * 256);
+    for (int j = 0; j < LPW; ++j)
+      if (j < c_loads) dma4(c_base, c_off[j] + (uint32_t)ks * 4, cbase + (j * 4 + gw) * 256);
   };
-  // B scales, one load per stage by group 1: a wave issues one only when no
-  // wave before it loads the same scales.  Scale bases are per tile,
-  // offsets small.
+  // fp32 B scales, one load per stage by group 1.  Scale bases are per
+  // tile, offsets small.
   uint32_t s_off = 0, s_lds = 0;
   const uint8_t* s_base = nullptr;
   bool s_load = false;
-  if (grp == 0) {
-  } else if constexpr (B_MX) {
-    s_load = gw < BN / 64;
-    const int cb = gw % (BN / 64);
-    s_base = sb8 + n0 * (K / 32);
-    s_off = (uint32_t)((cb * 64 + lane) * (K / 32));
-    s_lds = L::kA + L::kB + cb * 256;
+  if (grp == 0 || B_MX) {
   } else {
     // one fp32 scale per 128-column block and K step: one wave loads every
     // block's, lane l the scale of block l / SLB, so a block's scale is
@@ -366,12 +395,14 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmParams p) {
     else if (s_load)
       dma4(s_base, s_off + (uint32_t)kb * 4, sbase + s_lds);
   };
-  // a stage's loads; group 0 issues the A-scale chunk that starts at stage
-  // kb before them, so that the chunk has landed once the stage has
+  // a stage's loads, then the scale chunk that starts at stage kb: issued
+  // before any load of the next stage, it has landed once stage kb has
+  // (loads complete in order).  Issued last rather than first, the chunk's
+  // scattered rows do not delay the stage's data.
   auto issue = [&](int kb) {
-    if (grp == 0 && kb % SC == 0) issue_chunk(kb / SC);
 #pragma unroll
     for (int i = 0; i < PER; ++i) issue_one(kb, i);
+    if (kb % c_steps == 0) issue_chunk(kb / c_steps);
   };
 
   v4f acc[4][4];
@@ -395,11 +426,10 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmParams p) {
     const uint8_t* sA = smem + (kb % STAGES) * L::kStage;
     const uint8_t* sB = sA + L::kA;
     const uint32_t* sSB = reinterpret_cast<const uint32_t*>(sA + L::kA + L::kB);
-    // A scales of row r at step kb: sSC[(r / RPL) * 64 + r % RPL]
-    const uint32_t* sSC = reinterpret_cast<const uint32_t*>(smem + L::kRing + ((kb / SC) & 1) * L::kChunk) + (kb % SC) * RPL;
-    if constexpr (do_load) {
-      if (grp == 0 && (kb + STAGES - 1) % SC == 0) issue_chunk((kb + STAGES - 1) / SC);
-    }
+    // scales of A row r at step kb: sSCA[(r / RPLA) * 64 + r % RPLA], of B
+    // column c: sSCB[(c / RPLB) * 64 + c % RPLB]
+    const uint32_t* sSCA = reinterpret_cast<const uint32_t*>(smem + L::kRingA + ((kb / SCA) & 1) * L::kChunkA) + (kb % SCA) * RPLA;
+    const uint32_t* sSCB = reinterpret_cast<const uint32_t*>(smem + L::kRingB + ((kb / SCB) & 1) * L::kChunkB) + (kb % SCB) * RPLB;
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
       const int ar = wm * 64 + mi * 16 + fr;
@@ -408,10 +438,10 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmParams p) {
       af[mi] = make_frag(*reinterpret_cast<const u32x4*>(rowp + s0), *reinterpret_cast<const u32x4*>(rowp + (s0 ^ 64)));
       if constexpr (do_load) issue_one(kb + STAGES - 1, mi);
       if constexpr (A_MX) {
-        xa[mi] = (int)((sSC[(ar / RPL) * 64 + ar % RPL] >> (8 * fg)) & 0xFFu);
+        xa[mi] = (int)((sSCA[(ar / RPLA) * 64 + ar % RPLA] >> (8 * fg)) & 0xFFu);
       } else {
-        const int r0 = wm * 64 + mi * 16 + 4 * fg;   // 4 rows in one block of RPL (>= 16) rows
-        const u32x4 s4 = *reinterpret_cast<const u32x4*>(&sSC[(r0 / RPL) * 64 + r0 % RPL]);
+        const int r0 = wm * 64 + mi * 16 + 4 * fg;   // 4 rows in one block of RPLA (>= 16) rows
+        const u32x4 s4 = *reinterpret_cast<const u32x4*>(&sSCA[(r0 / RPLA) * 64 + r0 % RPLA]);
         sc[mi][0] = __uint_as_float(s4.x);
         sc[mi][1] = __uint_as_float(s4.y);
         sc[mi][2] = __uint_as_float(s4.z);
@@ -427,12 +457,15 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmParams p) {
       if constexpr (do_load) {
         if (4 + ni < PER) issue_one(kb + STAGES - 1, 4 + ni);
       }
-      if constexpr (B_MX) xb[ni] = (int)((sSB[bc] >> (8 * fg)) & 0xFFu);
+      if constexpr (B_MX) xb[ni] = (int)((sSCB[(bc / RPLB) * 64 + bc % RPLB] >> (8 * fg)) & 0xFFu);
     }
     if constexpr (MODE == kF32xF32) sbk = __uint_as_float(sSB[(wn >> 1) * SLB]);
     if constexpr (do_load) {
 #pragma unroll
       for (int i = 8; i < PER; ++i) issue_one(kb + STAGES - 1, i);
+    }
+    if constexpr (do_load) {
+      if ((kb + STAGES - 1) % c_steps == 0) issue_chunk((kb + STAGES - 1) / c_steps);
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the stage may be refilled after the next barrier
   };
