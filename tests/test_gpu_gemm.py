@@ -156,6 +156,29 @@ def test_grouped_edge_cases(bkind, n):
     assert np.array_equal(y16, codec.f32_to_bf16(y32))
 
 
+@pytest.mark.parametrize("n,k", [(256, 384), (384, 640), (256, 1152), (384, 128)])
+@pytest.mark.parametrize("bkind", ["1x32", "128x128"])
+def test_grouped_scale_chunk_tails(bkind, n, k):
+    """K steps (K / 128) that are not a multiple of the scale-chunk length
+    (4 steps, or 2 for 256x128 tiles with E8M0 B), with both tile shapes."""
+    sizes = [130, 0, 257, 64]
+    g = len(sizes)
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    total = int(off[-1])
+    aq, sa = _q(_rand_bf16((total, k), 1.0, 40 + k), "1x128")
+    bs = [_q(_rand_bf16((n, k), 0.02 * (e + 1), 50 + e), bkind) for e in range(g)]
+    bq = torch.stack([b[0] for b in bs]).contiguous()
+    sb = torch.stack([b[1] for b in bs]).contiguous()
+    offt = torch.from_numpy(off).cuda()
+    print(f"[grouped] scale-chunk tails {bkind} n={n} k={k}", flush=True)
+    y32 = _grouped(aq, sa, bq, sb, bkind, offt).cpu().numpy()
+    ref = gemm.grouped_gemm_ref(aq.cpu().numpy(), sa.cpu().numpy(), "1x128", bq.cpu().numpy(),
+                                sb.cpu().numpy(), bkind, off)
+    for e in range(g):
+        lo, hi = off[e], off[e + 1]
+        assert gemm.normwise_rel_err(y32[lo:hi], ref[e]) <= TOL, e
+
+
 @pytest.mark.parametrize("bkind", ["1x32", "128x128"])
 def test_grouped_many_groups(bkind):
     """1000 groups of random sizes 0..400 (a quarter of them empty): more
