@@ -77,13 +77,13 @@ __device__ __forceinline__ u32x4 ld16(const uint16_t* p) { return *reinterpret_c
 
 constexpr u32x4 kZero4 = {0u, 0u, 0u, 0u};
 
-__global__ __launch_bounds__(kPrepThreads) void lora_prep_kernel(LoraBwdParams p, int rp) {
-  const int64_t total = (int64_t)rp * p.n;
-  for (int64_t i = (int64_t)blockIdx.x * kPrepThreads + threadIdx.x; i < total; i += (int64_t)gridDim.x * kPrepThreads) {
-    const int c = (int)(i / p.n);
-    const int64_t n = i - (int64_t)c * p.n;
-    p.bt[i] = c < p.r ? p.lb[n * p.r + c] : (uint16_t)0;
-  }
+// Row c of the padded B^T (blockIdx.y = c < rp) is column c of B, zero for
+// c >= r; blockIdx.x covers n.
+__global__ __launch_bounds__(kPrepThreads) void lora_prep_kernel(LoraBwdParams p) {
+  const int c = (int)blockIdx.y;
+  const int64_t nn = (int64_t)blockIdx.x * kPrepThreads + threadIdx.x;
+  if (nn >= p.n) return;
+  p.bt[(int64_t)c * p.n + nn] = c < p.r ? p.lb[nn * p.r + c] : (uint16_t)0;
 }
 
 // P (blockIdx.y == 0: X_hat against A) or Q (blockIdx.y == 1: dY against
@@ -300,28 +300,35 @@ __global__ __launch_bounds__(kRedThreads) void lora_reduce_kernel(LoraBwdParams 
   }
 }
 
-__global__ __launch_bounds__(kFinThreads) void lora_finish_kernel(LoraBwdParams p, int rp) {
-  const int64_t eb = (int64_t)p.n * p.r, ea = (int64_t)p.r * p.k;
-  for (int64_t i = (int64_t)blockIdx.x * kFinThreads + threadIdx.x; i < eb + ea; i += (int64_t)gridDim.x * kFinThreads) {
-    float acc = 0.f;
-    if (i < eb) {
-      const int64_t n = i / p.r;
-      const int c = (int)(i - n * p.r);
-      for (int s = 0; s < p.slices; ++s) acc += p.part_b[((int64_t)s * p.n + n) * rp + c];
-      if (p.out_f32)
-        reinterpret_cast<float*>(p.d_b)[i] = acc;
-      else
-        reinterpret_cast<uint16_t*>(p.d_b)[i] = (uint16_t)(pack_bf16x2(acc, 0.f) & 0xFFFFu);
-    } else {
-      const int64_t e = i - eb;
-      const int c = (int)(e / p.k);
-      const int64_t kk = e - (int64_t)c * p.k;
-      for (int s = 0; s < p.slices; ++s) acc += p.part_a[((int64_t)s * rp + c) * p.k + kk];
-      if (p.out_f32)
-        reinterpret_cast<float*>(p.d_a)[e] = acc;
-      else
-        reinterpret_cast<uint16_t*>(p.d_a)[e] = (uint16_t)(pack_bf16x2(acc, 0.f) & 0xFFFFu);
-    }
+// Workgroups [0, nbb) sum dB: thread x is partial row x >> rp_log2 (= n),
+// rank x & (rp - 1) (rp is a power of two).  Workgroups nbb + c * kba + j
+// sum row c of dA, columns [kFinThreads * j, +kFinThreads).  Slices are
+// added in order, so the result does not depend on the launch.
+__global__ __launch_bounds__(kFinThreads) void lora_finish_kernel(LoraBwdParams p, int rp_log2, int nbb, int kba) {
+  const int rp = 1 << rp_log2;
+  float acc = 0.f;
+  if ((int)blockIdx.x < nbb) {
+    const int64_t x = (int64_t)blockIdx.x * kFinThreads + threadIdx.x;
+    const int64_t nn = x >> rp_log2;
+    const int c = (int)(x & (rp - 1));
+    if (nn >= p.n || c >= p.r) return;
+    for (int s = 0; s < p.slices; ++s) acc += p.part_b[(((int64_t)s * p.n + nn) << rp_log2) + c];
+    const int64_t o = nn * p.r + c;
+    if (p.out_f32)
+      reinterpret_cast<float*>(p.d_b)[o] = acc;
+    else
+      reinterpret_cast<uint16_t*>(p.d_b)[o] = (uint16_t)(pack_bf16x2(acc, 0.f) & 0xFFFFu);
+  } else {
+    const int b = (int)blockIdx.x - nbb;
+    const int c = b / kba;
+    const int64_t kk = (int64_t)(b - c * kba) * kFinThreads + threadIdx.x;
+    if (kk >= p.k) return;
+    for (int s = 0; s < p.slices; ++s) acc += p.part_a[((int64_t)s * rp + c) * p.k + kk];
+    const int64_t o = (int64_t)c * p.k + kk;
+    if (p.out_f32)
+      reinterpret_cast<float*>(p.d_a)[o] = acc;
+    else
+      reinterpret_cast<uint16_t*>(p.d_a)[o] = (uint16_t)(pack_bf16x2(acc, 0.f) & 0xFFFFu);
   }
 }
 
@@ -357,10 +364,10 @@ LoraPlan plan(int64_t m, int64_t n, int64_t k, int64_t r) {
 
 template <int CT>
 hipError_t launch_ct(const LoraBwdParams& p, const LoraPlan& pl, int num_cu, hipStream_t stream) {
+  (void)num_cu;
   if (pl.rp * (int64_t)p.n > 0) {
-    int64_t g = ((int64_t)pl.rp * p.n + kPrepThreads - 1) / kPrepThreads;
-    if (g > 4 * num_cu) g = 4 * num_cu;
-    hipLaunchKernelGGL(lora_prep_kernel, dim3((unsigned)g), dim3(kPrepThreads), 0, stream, p, pl.rp);
+    const int64_t g = ((int64_t)p.n + kPrepThreads - 1) / kPrepThreads;
+    hipLaunchKernelGGL(lora_prep_kernel, dim3((unsigned)g, (unsigned)pl.rp), dim3(kPrepThreads), 0, stream, p);
   }
   if (pl.mb > 0)
     hipLaunchKernelGGL((lora_proj_kernel<CT>), dim3(pl.mb, 2), dim3(kProjThreads), 0, stream, p);
@@ -369,9 +376,11 @@ hipError_t launch_ct(const LoraBwdParams& p, const LoraPlan& pl, int num_cu, hip
                        p, pl.cgb);
   const int64_t outs = (int64_t)p.r * (p.n + p.k);
   if (outs > 0) {
-    int64_t g = (outs + kFinThreads - 1) / kFinThreads;
-    if (g > 8 * num_cu) g = 8 * num_cu;
-    hipLaunchKernelGGL(lora_finish_kernel, dim3((unsigned)g), dim3(kFinThreads), 0, stream, p, pl.rp);
+    const int64_t nbb = ((int64_t)p.n * pl.rp + kFinThreads - 1) / kFinThreads;
+    const int64_t kba = ((int64_t)p.k + kFinThreads - 1) / kFinThreads;
+    const int rp_log2 = pl.rp == 16 ? 4 : pl.rp == 32 ? 5 : 6;
+    hipLaunchKernelGGL(lora_finish_kernel, dim3((unsigned)(nbb + (int64_t)p.r * kba)), dim3(kFinThreads), 0, stream, p,
+                       rp_log2, (int)nbb, (int)kba);
   }
   return hipGetLastError();
 }
