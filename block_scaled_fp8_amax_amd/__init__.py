@@ -142,12 +142,69 @@ def _contig(*ts):
             raise ValueError("fp8blk expects contiguous tensors")
 
 
+# The library takes raw device pointers and sizes and cannot see the
+# tensors behind them, so the binding checks what it can before a kernel
+# runs: every tensor on one GPU, the documented dtypes, and each buffer at
+# least as large as the sizes passed with it (floor-divided block counts:
+# shapes the library rejects never reach a kernel).
+_CODES = (torch.uint8, torch.float8_e4m3fn)
+_BF16 = (torch.bfloat16,)
+_F32 = (torch.float32,)
+_I32 = (torch.int32,)
+_U8 = (torch.uint8,)
+_OUT = (torch.bfloat16, torch.float32)
+
+
+def _same_gpu(where, *ts):
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{where}: every tensor must be on a GPU, got one on {t.device}")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{where}: tensors on different devices ({dev} and {t.device})")
+
+
+def _expect(where, name, t, dtypes, numel):
+    if t is None:
+        return
+    if t.dtype not in dtypes:
+        raise ValueError(f"{where}: {name} has dtype {t.dtype}, expected {' or '.join(str(d) for d in dtypes)}")
+    if t.numel() < numel:
+        raise ValueError(f"{where}: {name} holds {t.numel()} elements, needs at least {numel}")
+
+
+def _scale_numel(rows, cols, kind):
+    kind = _kind(kind)
+    if kind == FP8_BLOCK_1x32_E8M0:
+        return rows * (cols // 32), _U8
+    if kind == FP8_BLOCK_1x128_F32:
+        return rows * (cols // 128), _F32
+    return (rows // 128) * (cols // 128), _F32
+
+
+def _check_quantize_job(where, x, kind, q, scale, xdq):
+    if x.dim() != 2:
+        raise ValueError(f"{where}: x must be 2-D, got shape {tuple(x.shape)}")
+    rows, cols = x.shape
+    _expect(where, "x", x, _BF16, 0)
+    _expect(where, "q", q, _CODES, rows * cols)
+    sn, sdt = _scale_numel(rows, cols, kind)
+    _expect(where, "scale", scale, sdt, sn)
+    _expect(where, "xdq", xdq, _BF16, rows * cols)
+    _same_gpu(where, x, q, scale, xdq)
+
+
 # ------------------------------------------------------------- entry points
 
 def fp8_block_quantize(x, kind, rule, q, scale, xdq=None, stream=None):
     """x: bf16 [rows, cols]; q: uint8/float8_e4m3fn [rows, cols]; scale: uint8
     (1x32) or float32 of the kind's shape; xdq: optional bf16 [rows, cols]."""
     _contig(x, q, scale, xdq)
+    _check_quantize_job("fp8_block_quantize", x, kind, q, scale, xdq)
     rows, cols = x.shape
     st = library().fp8_block_quantize(_ptr(x), rows, cols, _kind(kind), _rule(rule), _ptr(q), _ptr(scale),
                                       _ptr(xdq), _stream(stream, x))
@@ -164,6 +221,9 @@ def fp8_block_quantize_batch(jobs, stream=None):
         x, kind, rule, q, scale = job[:5]
         xdq = job[5] if len(job) > 5 else None
         _contig(x, q, scale, xdq)
+        _check_quantize_job(f"fp8_block_quantize_batch job {i}", x, kind, q, scale, xdq)
+        if i and x.device != jobs[0][0].device:
+            raise ValueError("fp8_block_quantize_batch: jobs on different devices")
         rows, cols = x.shape
         arr[i] = QuantizeJob(_ptr(x), rows, cols, _kind(kind), _rule(rule), _ptr(q), _ptr(scale), _ptr(xdq))
     st = library().fp8_block_quantize_batch(arr, len(jobs), _stream(stream, jobs[0][0]))
@@ -174,7 +234,13 @@ def fp8_block_dequantize(q, scale, kind, x, stream=None):
     """q: uint8/float8_e4m3fn [rows, cols]; scale as written by
     fp8_block_quantize for ``kind``; x: bf16 [rows, cols] output."""
     _contig(q, scale, x)
+    where = "fp8_block_dequantize"
     rows, cols = q.shape
+    _expect(where, "q", q, _CODES, 0)
+    sn, sdt = _scale_numel(rows, cols, kind)
+    _expect(where, "scale", scale, sdt, sn)
+    _expect(where, "x", x, _BF16, rows * cols)
+    _same_gpu(where, q, scale, x)
     st = library().fp8_block_dequantize(_ptr(q), _ptr(scale), rows, cols, _kind(kind), _ptr(x), _stream(stream, q))
     _check(st, "fp8_block_dequantize")
 
@@ -183,8 +249,16 @@ def fp8_fake_quant_merge(w, lora_b, lora_a, q, scale, wdq=None, stream=None):
     """w: bf16 [n, k]; lora_b bf16 [n, r]; lora_a bf16 [r, k]; q [n, k];
     scale float32 [n/128, k/128]; wdq optional bf16 [n, k]."""
     _contig(w, lora_b, lora_a, q, scale, wdq)
+    where = "fp8_fake_quant_merge"
     n, k = w.shape
     r = lora_a.shape[0]
+    _expect(where, "w", w, _BF16, 0)
+    _expect(where, "lora_b", lora_b, _BF16, n * r)
+    _expect(where, "lora_a", lora_a, _BF16, r * k)
+    _expect(where, "q", q, _CODES, n * k)
+    _expect(where, "scale", scale, _F32, (n // 128) * (k // 128))
+    _expect(where, "wdq", wdq, _BF16, n * k)
+    _same_gpu(where, w, lora_b, lora_a, q, scale, wdq)
     st = library().fp8_fake_quant_merge(_ptr(w), _ptr(lora_b), _ptr(lora_a), n, k, r, _ptr(q), _ptr(scale),
                                         _ptr(wdq), _stream(stream, w))
     _check(st, "fp8_fake_quant_merge")
@@ -193,23 +267,46 @@ def fp8_fake_quant_merge(w, lora_b, lora_a, q, scale, wdq=None, stream=None):
 def fp8_block_scaled_gemm(a_q, a_scale, a_kind, b_q, b_scale, b_kind, y, stream=None):
     """Y[m, n] = deq(A) . deq(B)^T; y is bf16 or float32 [m, n]."""
     _contig(a_q, a_scale, b_q, b_scale, y)
+    where = "fp8_block_scaled_gemm"
     m, k = a_q.shape
     n = b_q.shape[0]
+    _expect(where, "a_q", a_q, _CODES, 0)
+    _expect(where, "b_q", b_q, _CODES, n * k)
+    sn, sdt = _scale_numel(m, k, a_kind)
+    _expect(where, "a_scale", a_scale, sdt, sn)
+    sn, sdt = _scale_numel(n, k, b_kind)
+    _expect(where, "b_scale", b_scale, sdt, sn)
+    _expect(where, "y", y, _OUT, m * n)
     y_type = FP8_OUT_F32 if y.dtype == torch.float32 else FP8_OUT_BF16
+    _same_gpu(where, a_q, a_scale, b_q, b_scale, y)
     st = library().fp8_block_scaled_gemm(_ptr(a_q), _ptr(a_scale), _kind(a_kind), _ptr(b_q), _ptr(b_scale),
                                          _kind(b_kind), m, n, k, _ptr(y), y_type, _stream(stream, a_q))
     _check(st, "fp8_block_scaled_gemm")
+
+
+def _check_grouped(where, a_q, a_scale, a_kind, a_rows, b_q, b_scale, b_kind, groups, n, k, offsets, y, total_m):
+    _expect(where, "a_q", a_q, _CODES, 0)
+    sn, sdt = _scale_numel(a_rows, k, a_kind)
+    _expect(where, "a_scale", a_scale, sdt, sn)
+    _expect(where, "b_q", b_q, _CODES, groups * n * k)
+    sn, sdt = _scale_numel(n, k, b_kind)
+    _expect(where, "b_scale", b_scale, sdt, groups * sn)
+    _expect(where, "group_offsets", offsets, _I32, groups + 1)
+    _expect(where, "y", y, _OUT, total_m * n)
 
 
 def fp8_grouped_gemm(a_q, a_scale, a_kind, b_q, b_scale, b_kind, group_offsets, y, stream=None):
     """a_q [total_m, k]; b_q [groups, n, k]; group_offsets int32 [groups+1]
     on the device; y bf16/float32 [total_m, n]."""
     _contig(a_q, a_scale, b_q, b_scale, group_offsets, y)
+    where = "fp8_grouped_gemm"
     total_m, k = a_q.shape
     groups, n = b_q.shape[0], b_q.shape[1]
     if group_offsets.dtype != torch.int32:
         raise ValueError("group_offsets must be int32")
+    _check_grouped(where, a_q, a_scale, a_kind, total_m, b_q, b_scale, b_kind, groups, n, k, group_offsets, y, total_m)
     y_type = FP8_OUT_F32 if y.dtype == torch.float32 else FP8_OUT_BF16
+    _same_gpu(where, a_q, a_scale, b_q, b_scale, group_offsets, y)
     st = library().fp8_grouped_gemm(_ptr(a_q), _ptr(a_scale), _kind(a_kind), _ptr(b_q), _ptr(b_scale),
                                     _kind(b_kind), _ptr(group_offsets), groups, total_m, n, k, _ptr(y), y_type,
                                     _stream(stream, a_q))
@@ -221,12 +318,15 @@ def fp8_grouped_gemm_gather(a_q, a_scale, a_kind, row_index, b_q, b_scale, b_kin
     grouped row); b_q [groups, n, k]; group_offsets int32 [groups+1];
     y bf16/float32 [total_m, n]."""
     _contig(a_q, a_scale, row_index, b_q, b_scale, group_offsets, y)
+    where = "fp8_grouped_gemm_gather"
     a_rows, k = a_q.shape
     groups, n = b_q.shape[0], b_q.shape[1]
     if group_offsets.dtype != torch.int32 or row_index.dtype != torch.int32:
         raise ValueError("group_offsets and row_index must be int32")
     total_m = row_index.numel()
+    _check_grouped(where, a_q, a_scale, a_kind, a_rows, b_q, b_scale, b_kind, groups, n, k, group_offsets, y, total_m)
     y_type = FP8_OUT_F32 if y.dtype == torch.float32 else FP8_OUT_BF16
+    _same_gpu(where, a_q, a_scale, row_index, b_q, b_scale, group_offsets, y)
     st = library().fp8_grouped_gemm_gather(_ptr(a_q), _ptr(a_scale), _kind(a_kind), a_rows, _ptr(row_index),
                                            _ptr(b_q), _ptr(b_scale), _kind(b_kind), _ptr(group_offsets), groups,
                                            total_m, n, k, _ptr(y), y_type, _stream(stream, a_q))
@@ -253,7 +353,13 @@ def fp8_lora_backward(dy, x, lora_b, lora_a, workspace, d_lora_b, d_lora_a, stre
         raise ValueError("fp8_lora_backward: inconsistent shapes")
     if d_lora_b.dtype != d_lora_a.dtype:
         raise ValueError("fp8_lora_backward: both gradients must have one dtype")
+    where = "fp8_lora_backward"
+    for name, t in (("dy", dy), ("x", x), ("lora_b", lora_b), ("lora_a", lora_a)):
+        _expect(where, name, t, _BF16, 0)
+    _expect(where, "d_lora_b", d_lora_b, _OUT, n * r)
+    _expect(where, "d_lora_a", d_lora_a, _OUT, r * k)
     out_type = FP8_OUT_F32 if d_lora_b.dtype == torch.float32 else FP8_OUT_BF16
+    _same_gpu(where, dy, x, lora_b, lora_a, workspace, d_lora_b, d_lora_a)
     st = library().fp8_lora_backward(_ptr(dy), _ptr(x), _ptr(lora_b), _ptr(lora_a), m, n, k, r, _ptr(workspace),
                                      workspace.numel() * workspace.element_size(), _ptr(d_lora_b), _ptr(d_lora_a),
                                      out_type, _stream(stream, dy))
@@ -267,7 +373,16 @@ def fp8_nvfp4_quantize(x, rows_per_tensor, q, block_scale, global_scale, tensor_
     global_scale, tensor_amax float32 [rows/rows_per_tensor] (tensor_amax is
     read instead of written when amax_given); xdq optional bf16 [rows, cols]."""
     _contig(x, q, block_scale, global_scale, tensor_amax, xdq)
+    where = "fp8_nvfp4_quantize"
     rows, cols = x.shape
+    tensors = rows // rows_per_tensor if rows_per_tensor > 0 else 0
+    _expect(where, "x", x, _BF16, 0)
+    _expect(where, "q", q, _U8, rows * (cols // 2))
+    _expect(where, "block_scale", block_scale, _CODES, rows * (cols // 16))
+    _expect(where, "global_scale", global_scale, _F32, tensors)
+    _expect(where, "tensor_amax", tensor_amax, _F32, tensors)
+    _expect(where, "xdq", xdq, _BF16, rows * cols)
+    _same_gpu(where, x, q, block_scale, global_scale, tensor_amax, xdq)
     st = library().fp8_nvfp4_quantize(_ptr(x), rows, cols, rows_per_tensor, _ptr(tensor_amax), 1 if amax_given else 0,
                                       _ptr(q), _ptr(block_scale), _ptr(global_scale), _ptr(xdq), _stream(stream, x))
     _check(st, "fp8_nvfp4_quantize")
@@ -277,7 +392,14 @@ def fp8_nvfp4_dequantize(q, block_scale, global_scale, rows_per_tensor, x, strea
     """q uint8 [rows, cols/2], block_scale [rows, cols/16], global_scale
     float32 [tensors]; x bf16 [rows, cols] output."""
     _contig(q, block_scale, global_scale, x)
+    where = "fp8_nvfp4_dequantize"
     rows, cols = x.shape
+    tensors = rows // rows_per_tensor if rows_per_tensor > 0 else 0
+    _expect(where, "q", q, _U8, rows * (cols // 2))
+    _expect(where, "block_scale", block_scale, _CODES, rows * (cols // 16))
+    _expect(where, "global_scale", global_scale, _F32, tensors)
+    _expect(where, "x", x, _BF16, rows * cols)
+    _same_gpu(where, q, block_scale, global_scale, x)
     st = library().fp8_nvfp4_dequantize(_ptr(q), _ptr(block_scale), _ptr(global_scale), rows, cols, rows_per_tensor,
                                         _ptr(x), _stream(stream, q))
     _check(st, "fp8_nvfp4_dequantize")

@@ -207,14 +207,76 @@ def test_lora_backward_validation(lib):
     assert call(db=A16 + 1) == ALIGN
 
 
-def test_python_binding_raises_with_status(lib):
+def test_python_binding_rejects_host_tensors(lib):
+    """Host tensors never reach the library: their pointers are not device
+    addresses.  (The status path of the binding is covered on the GPU.)"""
     import torch
-    x = torch.zeros((4, 48), dtype=torch.bfloat16)
-    q = torch.zeros((4, 48), dtype=torch.uint8)
-    s = torch.zeros((4, 1), dtype=torch.uint8)
-    with pytest.raises(fb.Fp8Error) as ei:
+    x = torch.zeros((4, 64), dtype=torch.bfloat16)
+    q = torch.zeros((4, 64), dtype=torch.uint8)
+    s = torch.zeros((4, 2), dtype=torch.uint8)
+    with pytest.raises(ValueError, match="on a GPU"):
         fb.fp8_block_quantize(x, "1x32", "ceil", q, s)
-    assert ei.value.status == SHAPE
+    w = torch.zeros((128, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="on a GPU"):
+        fb.fp8_block_scaled_gemm(q, torch.zeros((4, 1), dtype=torch.float32), "1x128",
+                                 torch.zeros((128, 64), dtype=torch.uint8), torch.zeros((1, 1), dtype=torch.float32),
+                                 "128x128", torch.zeros((4, 128), dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="on a GPU"):
+        fb.fp8_fake_quant_merge(w, torch.zeros((128, 4), dtype=torch.bfloat16),
+                                torch.zeros((4, 128), dtype=torch.bfloat16), torch.zeros((128, 128), dtype=torch.uint8),
+                                torch.zeros((1, 1), dtype=torch.float32))
+
+
+def test_python_binding_checks_dtypes_and_sizes(lib):
+    """Wrong dtypes and buffers smaller than the sizes passed with them are
+    refused before any device pointer is used (checked before the device)."""
+    import torch
+    bf, u8, f32 = torch.bfloat16, torch.uint8, torch.float32
+    x = torch.zeros((4, 256), dtype=bf)
+    q = torch.zeros((4, 256), dtype=u8)
+    with pytest.raises(ValueError, match="x has dtype"):
+        fb.fp8_block_quantize(x.float(), "1x128", "ceil", q, torch.zeros((4, 2), dtype=f32))
+    with pytest.raises(ValueError, match="q holds 512 elements"):
+        fb.fp8_block_quantize(x, "1x128", "ceil", torch.zeros((2, 256), dtype=u8), torch.zeros((4, 2), dtype=f32))
+    with pytest.raises(ValueError, match="scale has dtype"):
+        fb.fp8_block_quantize(x, "1x32", "ceil", q, torch.zeros((4, 8), dtype=f32))
+    with pytest.raises(ValueError, match="scale holds 7 elements"):
+        fb.fp8_block_quantize(x, "1x128", "ceil", q, torch.zeros((7,), dtype=f32))
+    with pytest.raises(ValueError, match="job 0: xdq"):
+        fb.fp8_block_quantize_batch([(x, "1x32", "ceil", q, torch.zeros((4, 8), dtype=u8), torch.zeros((4, 255), dtype=bf)),
+                                     (x, "1x128", "ceil", q, torch.zeros((4, 2), dtype=f32))])
+    with pytest.raises(ValueError, match="x holds"):
+        fb.fp8_block_dequantize(q, torch.zeros((4, 8), dtype=u8), "1x32", torch.zeros((4, 128), dtype=bf))
+    a = torch.zeros((8, 256), dtype=u8)
+    b = torch.zeros((256, 256), dtype=u8)
+    sa, sb = torch.zeros((8, 2), dtype=f32), torch.zeros((2, 2), dtype=f32)
+    with pytest.raises(ValueError, match="y holds"):
+        fb.fp8_block_scaled_gemm(a, sa, "1x128", b, sb, "128x128", torch.zeros((8, 255), dtype=bf))
+    with pytest.raises(ValueError, match="b_scale holds"):
+        fb.fp8_block_scaled_gemm(a, sa, "1x128", b, sb[:1], "128x128", torch.zeros((8, 256), dtype=bf))
+    with pytest.raises(ValueError, match="y has dtype"):
+        fb.fp8_block_scaled_gemm(a, sa, "1x128", b, sb, "128x128", torch.zeros((8, 256), dtype=torch.float16))
+    bg = torch.zeros((3, 256, 256), dtype=u8)
+    sbg = torch.zeros((3, 256, 8), dtype=u8)
+    offs = torch.zeros((4,), dtype=torch.int32)
+    with pytest.raises(ValueError, match="b_scale holds"):
+        fb.fp8_grouped_gemm(a, sa, "1x128", bg, sbg[:2], "1x32", offs, torch.zeros((8, 256), dtype=bf))
+    with pytest.raises(ValueError, match="group_offsets holds"):
+        fb.fp8_grouped_gemm(a, sa, "1x128", bg, sbg, "1x32", offs[:3], torch.zeros((8, 256), dtype=bf))
+    with pytest.raises(ValueError, match="y holds"):
+        fb.fp8_grouped_gemm_gather(a, sa, "1x128", torch.zeros((9,), dtype=torch.int32), bg, sbg, "1x32", offs,
+                                   torch.zeros((8, 256), dtype=bf))
+    with pytest.raises(ValueError, match="block_scale holds"):
+        fb.fp8_nvfp4_quantize(x, 4, torch.zeros((4, 128), dtype=u8), torch.zeros((4, 15), dtype=u8),
+                              torch.zeros((1,), dtype=f32), torch.zeros((1,), dtype=f32))
+    with pytest.raises(ValueError, match="global_scale holds"):
+        fb.fp8_nvfp4_dequantize(torch.zeros((4, 128), dtype=u8), torch.zeros((4, 16), dtype=u8),
+                                torch.zeros((0,), dtype=f32), 2, x)
+    dy, xx = torch.zeros((8, 128), dtype=bf), torch.zeros((8, 256), dtype=bf)
+    lb, la = torch.zeros((128, 4), dtype=bf), torch.zeros((4, 256), dtype=bf)
+    with pytest.raises(ValueError, match="d_lora_a holds"):
+        fb.fp8_lora_backward(dy, xx, lb, la, torch.zeros((1024,), dtype=u8), torch.zeros((128, 4), dtype=bf),
+                             torch.zeros((4, 255), dtype=bf))
 
 
 def test_routed_expert_name_rule():

@@ -287,3 +287,17 @@ def test_batch_dense_projection_pair_and_experts():
         torch.cuda.synchronize()
         for (x, kind, _, q, s), (q1, s1) in zip(jobs, ref):
             assert torch.equal(q, q1) and torch.equal(s.view(torch.uint8), s1.view(torch.uint8)), (kind, x.shape)
+
+
+def test_binding_raises_library_status():
+    """A shape the library rejects comes back as Fp8Error with its status
+    (1x32 blocks need cols % 32 == 0); nothing is enqueued."""
+    x = torch.zeros((4, 48), dtype=torch.bfloat16, device="cuda")
+    q = torch.zeros((4, 48), dtype=torch.uint8, device="cuda")
+    s = torch.zeros((4, 1), dtype=torch.uint8, device="cuda")
+    with pytest.raises(fb.Fp8Error) as ei:
+        fb.fp8_block_quantize(x, "1x32", "ceil", q, s)
+    assert ei.value.status == 2   # FP8_ERR_SHAPE
+    assert "shape" in str(ei.value).lower()
+    with pytest.raises(ValueError, match="on a GPU"):
+        fb.fp8_block_quantize(x, "1x32", "ceil", q.cpu(), s)
