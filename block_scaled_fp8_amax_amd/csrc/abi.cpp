@@ -204,8 +204,8 @@ static int grouped_common(const uint8_t* a_q, const void* a_scale, int a_kind, i
     return FP8_ERR_ALIGN;
   DeviceInfo* dev = nullptr;
   if (int s = current_device(&dev)) return s;
-  return hip_status(fp8blk::launch_grouped_gemm(a_q, a_scale, a_kind, gather ? row_index : nullptr, b_q, b_scale,
-                                                b_kind, group_offsets, groups, total_m, n, k, y,
+  return hip_status(fp8blk::launch_grouped_gemm(a_q, a_scale, a_kind, gather ? row_index : nullptr, a_rows, b_q,
+                                                b_scale, b_kind, group_offsets, groups, total_m, n, k, y,
                                                 y_type == FP8_OUT_F32, dev->num_cu,
                                                 reinterpret_cast<hipStream_t>(stream)));
 }

@@ -56,6 +56,7 @@ struct GemmParams {
   void* y;
   const int32_t* offsets;  // grouped only
   const int32_t* row_index; // grouped only: A row read for each grouped row (null = the row itself)
+  int64_t a_rows;           // gathered grouped only: rows of A (row_index values are clamped below it)
   int64_t m, n, k;
   int64_t b_group_stride;   // bytes of B per group
   int64_t sb_group_stride;  // scale elements of B per group
@@ -139,12 +140,27 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
 // (memory-bound) groups.  The grid is persistent: one workgroup per CU;
 // workgroup b (XCD b mod 8, slot b / 8) takes slot b / 8 of every window of
 // its XCD in turn.
+// The offsets are not checked on the host.  Group g's rows are taken as
+// [lo, hi) with lo = off[g] and hi = off[g+1] clamped into [0, total_m] and
+// hi >= lo, so offsets that break the contract give unspecified output rows
+// but no access outside A, its scales or Y.
+__device__ __forceinline__ int clamp_int(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
+__device__ __forceinline__ void group_rows(const GemmParams& p, int g, int* lo, int* hi) {
+  const int total = (int)p.m;
+  *lo = clamp_int(p.offsets[g], 0, total);
+  *hi = clamp_int(p.offsets[g + 1], *lo, total);
+}
+
 // s_pref: LDS of groups + 1 ints; returns the tile count.
 template <int BM>
 __device__ __forceinline__ int grouped_prefix(const GemmParams& p, int* s_pref, int nthreads) {
   const int groups = p.groups;
   const int t = threadIdx.x;
-  for (int g = t; g < groups; g += nthreads) s_pref[g + 1] = (p.offsets[g + 1] - p.offsets[g] + BM - 1) / BM;
+  for (int g = t; g < groups; g += nthreads) {
+    int lo, hi;
+    group_rows(p, g, &lo, &hi);
+    s_pref[g + 1] = (hi - lo + BM - 1) / BM;
+  }
   if (t == 0) s_pref[0] = 0;
   __syncthreads();
   for (int d = 1; d < groups; d <<= 1) {  // inclusive scan of s_pref[1..groups]
@@ -180,8 +196,10 @@ __device__ __forceinline__ void grouped_locate(const GemmParams& p, const int* s
   const int tm = b * band + rr % rows_here;
   *g_out = g;
   *tn_out = rr / rows_here;
-  *row0 = (int64_t)p.offsets[g] + (int64_t)tm * BM;
-  const int64_t left = (int64_t)p.offsets[g + 1] - *row0;
+  int row_lo, row_hi;
+  group_rows(p, g, &row_lo, &row_hi);
+  *row0 = (int64_t)row_lo + (int64_t)tm * BM;
+  const int64_t left = (int64_t)row_hi - *row0;
   *rows = (int)(left < BM ? left : BM);
 }
 
@@ -306,7 +324,9 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmParams p) {
   // problem, row row_index[m0 + r] (offsets then count from A's base; the
   // library checks that A's rows * K fit in 32 bits).
   const bool gather = GROUPED && p.row_index != nullptr;
-  auto a_row = [&](int r) -> int64_t { return gather ? (int64_t)p.row_index[m0 + r] : (int64_t)r; };
+  auto a_row = [&](int r) -> int64_t {
+    return gather ? (int64_t)clamp_int(p.row_index[m0 + r], 0, (int)p.a_rows - 1) : (int64_t)r;
+  };
   const uint8_t* aq = gather ? p.a : p.a + m0 * K;
   const uint8_t* bt = bq + n0 * K;
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
@@ -663,7 +683,7 @@ hipError_t launch_gemm(const uint8_t* a, const void* sa, int a_kind, const uint8
 }
 
 hipError_t launch_grouped_gemm(const uint8_t* a, const void* sa, int a_kind, const int32_t* row_index,
-                               const uint8_t* b, const void* sb, int b_kind, const int32_t* offsets, int64_t groups,
+                               int64_t a_rows, const uint8_t* b, const void* sb, int b_kind, const int32_t* offsets, int64_t groups,
                                int64_t total_m, int64_t n, int64_t k, void* y, bool out_f32, int num_cu,
                                hipStream_t stream) {
   (void)a_kind;
@@ -671,6 +691,7 @@ hipError_t launch_grouped_gemm(const uint8_t* a, const void* sa, int a_kind, con
   p.a = a; p.sa = sa; p.b = b; p.sb = sb; p.y = y;
   p.offsets = offsets;
   p.row_index = row_index;
+  p.a_rows = a_rows;
   p.m = total_m; p.n = n; p.k = k;
   p.groups = (int)groups;
   p.b_group_stride = n * k;

@@ -45,7 +45,7 @@ hipError_t launch_merge(const uint16_t* w, const uint16_t* lb, const uint16_t* l
 hipError_t launch_gemm(const uint8_t* a, const void* sa, int a_kind, const uint8_t* b, const void* sb, int b_kind,
                        int64_t m, int64_t n, int64_t k, void* y, bool out_f32, int num_cu, hipStream_t stream);
 hipError_t launch_grouped_gemm(const uint8_t* a, const void* sa, int a_kind, const int32_t* row_index,
-                               const uint8_t* b, const void* sb, int b_kind, const int32_t* offsets, int64_t groups,
+                               int64_t a_rows, const uint8_t* b, const void* sb, int b_kind, const int32_t* offsets, int64_t groups,
                                int64_t total_m, int64_t n, int64_t k, void* y, bool out_f32, int num_cu,
                                hipStream_t stream);
 

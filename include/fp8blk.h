@@ -228,7 +228,10 @@ int fp8_block_scaled_gemm(const uint8_t* a_q, const void* a_scale, int a_kind,
  *     [groups][n][k/32]) or FP8_BLOCK_128x128_F32 (float
  *     [groups][n/128][k/128]);
  * group_offsets: DEVICE int32 [groups+1], off[0] = 0, non-decreasing,
- *     off[groups] = total_m (not checked: a violation is undefined);
+ *     off[groups] = total_m.  Not checked on the host; the kernel clamps
+ *     each group's rows into [0, total_m] (and empty where off[g+1] <
+ *     off[g]), so a violation leaves output rows unspecified but accesses
+ *     nothing outside the buffers;
  * y [total_m x n] out, bf16 or float per y_type (16-byte aligned).
  * Shape: 1 <= groups <= 1024, 0 <= total_m < 2^31, n % 128 == 0,
  *        k % 128 == 0, 0 < k <= 2^24.
@@ -254,8 +257,10 @@ int fp8_grouped_gemm(const uint8_t* a_q, const void* a_scale, int a_kind,
  * writing that permuted copy.
  * a_q [a_rows x k] codes, a_kind = FP8_BLOCK_1x128_F32 (float scales
  *     [a_rows][k/128]); a_rows * k < 2^32.
- * row_index: DEVICE int32 [total_m], values in [0, a_rows) (not checked: a
- *     violation is undefined); 4-byte aligned.
+ * row_index: DEVICE int32 [total_m], values in [0, a_rows); 4-byte
+ *     aligned.  Not checked on the host; the kernel clamps each value into
+ *     [0, a_rows), so a violation gives unspecified rows but no access
+ *     outside A or its scales.
  * Every other argument as for fp8_grouped_gemm.
  */
 int fp8_grouped_gemm_gather(const uint8_t* a_q, const void* a_scale, int a_kind, int64_t a_rows,
