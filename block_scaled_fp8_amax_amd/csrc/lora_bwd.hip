@@ -43,7 +43,7 @@ namespace {
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 constexpr int kPrepThreads = 256;
-constexpr int kProjThreads = 256;   // 4 waves, 32 tokens
+constexpr int kProjThreads = 256;   // 4 waves, 32 tokens (ranks above 16; rank <= 16: 8 waves, 64 tokens)
 constexpr int kRedThreads = 512;    // 4 column waves x 2 row groups
 constexpr int kRedCols = 512;       // columns per reduction workgroup
 constexpr int kFinThreads = 256;
@@ -87,10 +87,12 @@ __global__ __launch_bounds__(kPrepThreads) void lora_prep_kernel(LoraBwdParams p
 }
 
 // P (blockIdx.y == 0: X_hat against A) or Q (blockIdx.y == 1: dY against
-// B^T) for tokens [32 * blockIdx.x, +32).
-template <int CT>
-__global__ __launch_bounds__(kProjThreads) void lora_proj_kernel(LoraBwdParams p) {
-  __shared__ float red[4][2][CT][4][64];
+// B^T) for tokens [16 T * blockIdx.x, +16 T): NWV waves, each T 16-token
+// tiles over the 128-wide blocks w, w + NWV, ... of the hidden dimension.
+template <int CT, int T>
+__global__ __launch_bounds__(T == 4 ? 512 : 256) void lora_proj_kernel(LoraBwdParams p) {
+  constexpr int NWV = T == 4 ? 8 : 4;
+  __shared__ float red[NWV][T][CT][4][64];
   const bool isq = blockIdx.y != 0;
   const uint16_t* src = isq ? p.dy : p.x;
   const int64_t ld = isq ? p.n : p.k;
@@ -99,16 +101,16 @@ __global__ __launch_bounds__(kProjThreads) void lora_proj_kernel(LoraBwdParams p
   u32x4* frag = isq ? p.qf : p.pf;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int fr = lane & 15, fg = lane >> 4;
-  const int64_t m0 = (int64_t)blockIdx.x * 32;
+  const int64_t m0 = (int64_t)blockIdx.x * (16 * T);
   const int nkb = (int)(ld / 128);
 
   // Lane (fr, fg) of tile t reads token m0 + 16t + fr; of fragment ct, row
   // 16ct + fr of the small operand.  MFMA j of a 128-wide block covers
   // hidden indices 32j + 8fg + e, e = 0..7, in both operands.
-  const uint16_t* xr[2];
-  bool xv[2];
+  const uint16_t* xr[T];
+  bool xv[T];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
+  for (int t = 0; t < T; ++t) {
     const int64_t row = m0 + 16 * t + fr;
     xv[t] = row < p.m;
     xr[t] = src + (xv[t] ? row : 0) * ld + 8 * fg;
@@ -122,16 +124,16 @@ __global__ __launch_bounds__(kProjThreads) void lora_proj_kernel(LoraBwdParams p
     sr[ct] = sm + (int64_t)(sv[ct] ? c : 0) * ld + 8 * fg;
   }
 
-  v4f acc[2][CT];
+  v4f acc[T][CT];
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
+  for (int t = 0; t < T; ++t)
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) acc[t][ct] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-  u32x4 xa[2][4], sa[CT][4];
+  u32x4 xa[T][4], sa[CT][4];
   auto load = [&](int kb) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < T; ++t)
 #pragma unroll
       for (int j = 0; j < 4; ++j) xa[t][j] = xv[t] ? ld16(xr[t] + kb * 128 + 32 * j) : kZero4;
 #pragma unroll
@@ -142,28 +144,28 @@ __global__ __launch_bounds__(kProjThreads) void lora_proj_kernel(LoraBwdParams p
   int kb = w;
   if (kb < nkb) load(kb);
   while (kb < nkb) {
-    u32x4 xc[2][4], sc[CT][4];
+    u32x4 xc[T][4], sc[CT][4];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < T; ++t)
 #pragma unroll
       for (int j = 0; j < 4; ++j) xc[t][j] = xa[t][j];
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
       for (int j = 0; j < 4; ++j) sc[ct][j] = sa[ct][j];
-    kb += 4;
+    kb += NWV;
     if (kb < nkb) load(kb);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < T; ++t)
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) acc[t][ct] = mfma_bf16(xc[t][j], sc[ct][j], acc[t][ct]);
   }
 
   // acc[t][ct] lane l holds token m0 + 16t + 4(l/16) + v, column 16ct + l%16.
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
+  for (int t = 0; t < T; ++t)
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
@@ -172,21 +174,28 @@ __global__ __launch_bounds__(kProjThreads) void lora_proj_kernel(LoraBwdParams p
 
   // Fragment lane L = (column L%16, group L/16) holds tokens 8(L/16) + e of
   // the block, e = 0..7; thread (L, ep) forms elements 2ep and 2ep + 1.
-  const int L = threadIdx.x & 63, ep = threadIdx.x >> 6;
+  // With T = 4 the workgroup writes two 32-token blocks: waves 4b .. 4b+3
+  // form block b.
+  const int L = threadIdx.x & 63, ep = (threadIdx.x >> 6) & 3, b = (threadIdx.x >> 6) >> 2;
   const int cc = L & 15, G = L >> 4;
+  const int64_t blk = (int64_t)blockIdx.x * (T / 2) + b;
+  if (blk >= p.mb) return;
   uint32_t* fw = reinterpret_cast<uint32_t*>(frag);
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) {
     float s[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int ml = 8 * G + 2 * ep + h;
+      const int ml = 32 * b + 8 * G + 2 * ep + h;
       const int t = ml >> 4, g = (ml & 15) >> 2, v = ml & 3, sl = 16 * g + cc;
-      s[h] = ((red[0][t][ct][v][sl] + red[1][t][ct][v][sl]) + red[2][t][ct][v][sl]) + red[3][t][ct][v][sl];
+      float a = red[0][t][ct][v][sl];
+#pragma unroll
+      for (int ww = 1; ww < NWV; ++ww) a += red[ww][t][ct][v][sl];
+      s[h] = a;
     }
     const uint32_t hi = pack_bf16x2(s[0], s[1]);
     const uint32_t lo = pack_bf16x2(s[0] - bf_lo(hi), s[1] - bf_hi(hi));
-    const int64_t base = (((int64_t)blockIdx.x * CT + ct) * 2) * 256 + L * 4 + ep;
+    const int64_t base = ((blk * CT + ct) * 2) * 256 + L * 4 + ep;
     fw[base] = hi;
     fw[base + 256] = lo;
   }
@@ -370,7 +379,12 @@ hipError_t launch_ct(const LoraBwdParams& p, const LoraPlan& pl, int num_cu, hip
     hipLaunchKernelGGL(lora_prep_kernel, dim3((unsigned)g, (unsigned)pl.rp), dim3(kPrepThreads), 0, stream, p);
   }
   if (pl.mb > 0)
-    hipLaunchKernelGGL((lora_proj_kernel<CT>), dim3(pl.mb, 2), dim3(kProjThreads), 0, stream, p);
+  {
+    if constexpr (CT == 1)
+      hipLaunchKernelGGL((lora_proj_kernel<CT, 4>), dim3((pl.mb + 1) / 2, 2), dim3(512), 0, stream, p);
+    else
+      hipLaunchKernelGGL((lora_proj_kernel<CT, 2>), dim3(pl.mb, 2), dim3(kProjThreads), 0, stream, p);
+  }
   if (pl.cgb + pl.cga > 0)
     hipLaunchKernelGGL((lora_reduce_kernel<CT>), dim3((pl.cgb + pl.cga) * pl.slices), dim3(kRedThreads), 0, stream,
                        p, pl.cgb);

@@ -66,6 +66,7 @@ def _inputs(m, n, k, r, seed):
     (64, 512, 512, 64),
     (4096, 512, 640, 16),       # many token slices
     (1000, 1024, 256, 8),
+    (80, 256, 384, 12),         # rank <= 16 runs 64 tokens per projection workgroup: odd count of 32-token blocks
 ])
 def test_small_shapes(m, n, k, r, out):
     print(f"[lora_bwd] m={m} n={n} k={k} r={r} {out}", flush=True)
