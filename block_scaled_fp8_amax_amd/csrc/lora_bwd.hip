@@ -43,7 +43,7 @@ namespace {
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 constexpr int kPrepThreads = 256;
-constexpr int kProjThreads = 256;   // 4 waves, 32 tokens (ranks above 16; rank <= 16: 8 waves, 64 tokens)
+constexpr int kProjThreads = 256;   // 4 waves, 32 tokens (ranks above 32; rank <= 32: 8 waves, 64 tokens)
 constexpr int kRedThreads = 512;    // 4 column waves x 2 row groups
 constexpr int kRedCols = 512;       // columns per reduction workgroup
 constexpr int kFinThreads = 256;
@@ -380,7 +380,7 @@ hipError_t launch_ct(const LoraBwdParams& p, const LoraPlan& pl, int num_cu, hip
   }
   if (pl.mb > 0)
   {
-    if constexpr (CT == 1)
+    if constexpr (CT <= 2)
       hipLaunchKernelGGL((lora_proj_kernel<CT, 4>), dim3((pl.mb + 1) / 2, 2), dim3(512), 0, stream, p);
     else
       hipLaunchKernelGGL((lora_proj_kernel<CT, 2>), dim3(pl.mb, 2), dim3(kProjThreads), 0, stream, p);
