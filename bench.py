@@ -402,6 +402,47 @@ def prequant_nvfp4_workload(fb, dev):
                     dtype="fp4")
 
 
+def dequant_nvfp4_workload(fb, dev):
+    """NVFP4 MoE layer back to bf16: the packed codes, e4m3 block scales and
+    per-tensor scales of the NVFP4 prequant workload (quantized while
+    setting up) are dequantized, one call per stacked shape."""
+    import workloads
+    E, I, H = 256, 2048, 7168
+    fac = workloads.expert_factors()
+    guq = torch.empty((E * 2 * I, H // 2), dtype=torch.uint8, device=dev)
+    gus = torch.empty((E * 2 * I, H // 16), dtype=torch.uint8, device=dev)
+    gug = torch.empty((2 * E,), dtype=torch.float32, device=dev)
+    dnq = torch.empty((E * H, I // 2), dtype=torch.uint8, device=dev)
+    dns = torch.empty((E * H, I // 16), dtype=torch.uint8, device=dev)
+    dng = torch.empty((E,), dtype=torch.float32, device=dev)
+    amax = torch.empty((2,), dtype=torch.float32, device=dev)
+    for e in range(E):
+        gate, up, down = workloads.expert_weights(e, dev, fac)
+        for j, wt in enumerate((gate, up)):
+            r0 = e * 2 * I + j * I
+            fb.fp8_nvfp4_quantize(wt, I, guq[r0:r0 + I], gus[r0:r0 + I], gug[2 * e + j:2 * e + j + 1], amax[:1])
+        fb.fp8_nvfp4_quantize(down, H, dnq[e * H:(e + 1) * H], dns[e * H:(e + 1) * H], dng[e:e + 1], amax[1:])
+        del gate, up, down
+    gux = torch.empty((E * 2 * I, H), dtype=torch.bfloat16, device=dev)
+    dnx = torch.empty((E * H, I), dtype=torch.bfloat16, device=dev)
+
+    def launches(i):
+        return [("nvfp4_dequantize_gate_up", lambda: fb.fp8_nvfp4_dequantize(guq, gus, gug, I, gux)),
+                ("nvfp4_dequantize_down", lambda: fb.fp8_nvfp4_dequantize(dnq, dns, dng, H, dnx))]
+
+    # algorithmic bytes: packed codes (1/2 B) and block scales (1/16 B) read,
+    # bf16 written, per element
+    n_gu, n_dn = gux.numel(), dnx.numel()
+    kbytes = {"nvfp4_dequantize_gate_up": n_gu * 2 + n_gu // 2 + n_gu // 16 + 2 * E * 4,
+              "nvfp4_dequantize_down": n_dn * 2 + n_dn // 2 + n_dn // 16 + E * 4}
+    cfg = {"workload": "NVFP4 MoE layer to bf16: 256 experts x {gate, up 2048x7168; down 7168x2048} packed E2M1 "
+                       "codes + e4m3 1x16 block scales + one fp32 scale per expert projection -> bf16 (22.5 GB "
+                       "written); experts stacked per shape, one call per shape",
+           "experts": E, "elements": n_gu + n_dn, "tensors": 3 * E}
+    return Workload(launches, "nvfp4_dequantize_gate_up", "hbm", 0.0, sum(kbytes.values()), kbytes, {}, cfg,
+                    "GB/s", dtype="fp4")
+
+
 def qat_backward_workload(fb, dev):
     """QAT backward for the LoRA factors of the qat step: dB [7168 x 16] and
     dA [16 x 7168] from the output gradient dY 8192x7168 and the
@@ -438,7 +479,7 @@ def qat_backward_workload(fb, dev):
 WORKLOADS = {"dense": dense_workload, "mx": mx_workload, "qat": qat_workload, "prequant": prequant_workload,
              "moe": moe_workload, "moe_gather": moe_gather_workload, "moe_down": moe_down_workload,
              "dequant": dequant_workload, "qat_backward": qat_backward_workload,
-             "prequant_nvfp4": prequant_nvfp4_workload}
+             "prequant_nvfp4": prequant_nvfp4_workload, "dequant_nvfp4": dequant_nvfp4_workload}
 
 
 # ------------------------------------------------------------ traffic record
@@ -450,6 +491,7 @@ _TRAFFIC_SOURCES = {
     "moe": ("gemm.hip", "device.h"), "moe_gather": ("gemm.hip", "device.h"), "moe_down": ("gemm.hip", "device.h"),
     "prequant": ("quantize.hip", "device.h"), "dequant": ("dequant.hip", "device.h"),
     "qat_backward": ("lora_bwd.hip", "device.h"), "prequant_nvfp4": ("nvfp4.hip", "device.h"),
+    "dequant_nvfp4": ("nvfp4.hip", "device.h"),
 }
 
 
@@ -611,7 +653,7 @@ def cpu_baseline_qat_backward(rows=2048):
                       f"formed; {secs:.2f} s"}
 
 
-def cpu_baseline_nvfp4():
+def cpu_baseline_nvfp4(dequant=False):
     """The oracle on one expert's gate projection (2048x7168), about 1/768
     of the MoE layer's elements."""
     import workloads
@@ -619,9 +661,15 @@ def cpu_baseline_nvfp4():
     gate, _, _ = workloads.expert_weights(0, "cpu")
     gb = workloads.bf16_bits(gate)
     n = gb.size
-    (_, secs) = _timed(lambda: onv.quantize(gb))
+    if dequant:
+        packed, bs, g, _, _ = onv.quantize(gb)
+        (_, secs) = _timed(lambda: onv.dequantize(packed, bs, g, gb.shape[0]))
+        what = "dequantize"
+    else:
+        (_, secs) = _timed(lambda: onv.quantize(gb))
+        what = "quantize"
     return {"value": (n * 2 + n / 2 + n / 16) / secs / 1e9, "unit": "GB/s", "cores": _oracle_threads(),
-            "kind": "oracle", "sample": f"NVFP4 quantize of expert 0's gate projection 2048x7168; {secs:.2f} s"}
+            "kind": "oracle", "sample": f"NVFP4 {what} of expert 0's gate projection 2048x7168; {secs:.2f} s"}
 
 
 CPU_BASELINES = {
@@ -634,7 +682,8 @@ CPU_BASELINES = {
     "moe_gather": lambda: cpu_baseline_grouped(),
     "moe_down": lambda: cpu_baseline_grouped(n=7168, k=2048, down=True),
     "qat_backward": lambda: cpu_baseline_qat_backward(),
-    "prequant_nvfp4": cpu_baseline_nvfp4,
+    "prequant_nvfp4": lambda: cpu_baseline_nvfp4(False),
+    "dequant_nvfp4": lambda: cpu_baseline_nvfp4(True),
 }
 
 
