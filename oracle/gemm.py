@@ -16,11 +16,14 @@ What the GEMM computes (reading, listed in the design doc): Y = A_hat . B_hat^T
 with both operands stored K-contiguous ([M, K] and [N, K]), where
 A_hat = RN32(decode(qa) * sa) and B_hat = RN32(decode(qb) * sb) are the
 dequantized fp32 operands (exact for E8M0 scales).  The reference result is
-the fp32-accumulated product of those dequantized operands; the library
-fp32 matmul (numpy / BLAS sgemm) is that step.  A float64 product of the
-same operands is kept for information.  The grouped GEMM is the dense
-GEMM applied per group: group g owns rows [off[g], off[g+1]) of A and the
-expert matrix B[g].
+the fp32-accumulated product of those dequantized operands, written out as
+its plain definition: for every output, the fp32 sum of the rounded
+products RN32(A_hat[m, k] * B_hat[n, k]) taken in the order k = 0..K-1,
+starting from 0 (no blocking, no fused multiply-add).  A float64 product
+of the same operands (a library matmul: its rounding is far below the
+tolerance) is the near-exact value it is compared with.  The grouped GEMM
+is the dense GEMM applied per group: group g owns rows [off[g], off[g+1])
+of A and the expert matrix B[g].
 """
 
 import numpy as np
@@ -33,15 +36,36 @@ def dequant_operand(q, scale, kind):
     return dequantize_f32(np.asarray(q, dtype=np.uint8), scale, kind)
 
 
+def sum_k_ordered(a_hat, b_hat):
+    """Y[m, n] = (((0 + p_0) + p_1) + ...) + p_{K-1} in float32, with
+    p_k = RN32(a_hat[m, k] * b_hat[n, k]).  Each step is one numpy float32
+    operation (rounded on its own); rows are taken 64 at a time only to keep
+    the running sums small, which does not change any sum."""
+    a = np.asarray(a_hat, dtype=np.float32)
+    b = np.asarray(b_hat, dtype=np.float32)
+    m, k = a.shape
+    n = b.shape[0]
+    bt = np.ascontiguousarray(b.T)                 # [K, N]: row k holds b_hat[:, k]
+    out = np.empty((m, n), dtype=np.float32)
+    for r0 in range(0, m, 64):
+        at = np.ascontiguousarray(a[r0:r0 + 64].T)  # [K, rows]
+        acc = np.zeros((at.shape[1], n), dtype=np.float32)
+        for t in range(k):
+            acc += np.multiply.outer(at[t], bt[t])
+        out[r0:r0 + 64] = acc
+    return out
+
+
 def gemm_ref32(a_q, a_scale, a_kind, b_q, b_scale, b_kind):
-    """fp32-accumulated Y[M, N] = A_hat . B_hat^T (library fp32 matmul)."""
+    """fp32-accumulated Y[M, N] = A_hat . B_hat^T, k-ordered (sum_k_ordered)."""
     a = dequant_operand(a_q, a_scale, a_kind)
     b = dequant_operand(b_q, b_scale, b_kind)
-    return np.matmul(a, b.T)
+    return sum_k_ordered(a, b)
 
 
 def gemm_ref64(a_q, a_scale, a_kind, b_q, b_scale, b_kind):
-    """The same product accumulated in float64 (informational)."""
+    """The same product accumulated in float64 (library matmul; rounding
+    about 2^-53 per term, so it stands for the exact product here)."""
     a = dequant_operand(a_q, a_scale, a_kind).astype(np.float64)
     b = dequant_operand(b_q, b_scale, b_kind).astype(np.float64)
     return np.matmul(a, b.T)
@@ -78,7 +102,7 @@ def grouped_gemm_ref(a_q, a_scale, a_kind, b_q, b_scale, b_kind, offsets,
         if acc64:
             out[g] = np.matmul(a.astype(np.float64), b.astype(np.float64).T)
         else:
-            out[g] = np.matmul(a, b.T)
+            out[g] = sum_k_ordered(a, b)
     return out
 
 

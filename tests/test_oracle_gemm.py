@@ -41,6 +41,28 @@ def test_tiny_gemm_against_exact_rationals():
                 assert abs(float(y32[i, j]) - float(ex)) <= k * 2.0 ** -24 * absum * 1.01
 
 
+def test_ref32_sums_in_k_order():
+    """The fp32 reference adds the rounded products in the order k = 0..K-1:
+    with products 1, 2^24, -2^24 (in that order) the running sum rounds
+    1 + 2^24 to 2^24 (ties to even) and ends at 0, where any other order of
+    the same three terms, or float64, gives 1.  The operands are MXFP8: code
+    0x38 is 1.0 and 0xB8 is -1.0; E8M0 code 127 + X scales by 2^X."""
+    k = 96
+    aq = np.zeros((1, k), np.uint8)
+    bq = np.zeros((1, k), np.uint8)
+    aq[0, [0, 32, 64]] = [0x38, 0x38, 0xB8]
+    bq[0, [0, 32, 64]] = 0x38
+    sa = np.array([[127, 127 + 24, 127 + 24]], np.uint8)
+    sb = np.full((1, 3), 127, np.uint8)
+    assert gemm.gemm_ref32(aq, sa, "1x32", bq, sb, "1x32")[0, 0] == 0.0
+    assert gemm.gemm_ref64(aq, sa, "1x32", bq, sb, "1x32")[0, 0] == 1.0
+    # the later term first: 2^24 + (-2^24) + 1 = 1 in any precision
+    aq2 = aq.copy()
+    aq2[0, [0, 64]] = aq[0, [64, 0]]
+    sa2 = np.array([[127 + 24, 127 + 24, 127]], np.uint8)
+    assert gemm.gemm_ref32(aq2, sa2, "1x32", bq, sb, "1x32")[0, 0] == 1.0
+
+
 def test_dequantized_operand_is_code_times_scale():
     aq, as_ = _quantized(4, 256, "1x128", 3)
     ahat = gemm.dequant_operand(aq, as_, "1x128")
