@@ -177,6 +177,26 @@ def _expect(where, name, t, dtypes, numel):
         raise ValueError(f"{where}: {name} holds {t.numel()} elements, needs at least {numel}")
 
 
+def _expect_dims(where, name, t, shape):
+    """A tensor with as many dimensions as ``shape`` must have exactly that
+    shape: the library reads it with the strides the sizes imply, so a
+    wider row would be read wrongly.  A buffer given with another number of
+    dimensions (for example flat) is checked by size only."""
+    if t is None or t.dim() != len(shape):
+        return
+    if tuple(t.shape) != tuple(int(d) for d in shape):
+        raise ValueError(f"{where}: {name} has shape {tuple(t.shape)}, expected {tuple(int(d) for d in shape)}")
+
+
+def _scale_dims(rows, cols, kind):
+    kind = _kind(kind)
+    if kind == FP8_BLOCK_1x32_E8M0:
+        return (rows, cols // 32)
+    if kind == FP8_BLOCK_1x128_F32:
+        return (rows, cols // 128)
+    return (rows // 128, cols // 128)
+
+
 def _scale_numel(rows, cols, kind):
     kind = _kind(kind)
     if kind == FP8_BLOCK_1x32_E8M0:
@@ -195,6 +215,9 @@ def _check_quantize_job(where, x, kind, q, scale, xdq):
     sn, sdt = _scale_numel(rows, cols, kind)
     _expect(where, "scale", scale, sdt, sn)
     _expect(where, "xdq", xdq, _BF16, rows * cols)
+    _expect_dims(where, "q", q, (rows, cols))
+    _expect_dims(where, "scale", scale, _scale_dims(rows, cols, kind))
+    _expect_dims(where, "xdq", xdq, (rows, cols))
     _same_gpu(where, x, q, scale, xdq)
 
 
@@ -240,6 +263,8 @@ def fp8_block_dequantize(q, scale, kind, x, stream=None):
     sn, sdt = _scale_numel(rows, cols, kind)
     _expect(where, "scale", scale, sdt, sn)
     _expect(where, "x", x, _BF16, rows * cols)
+    _expect_dims(where, "scale", scale, _scale_dims(rows, cols, kind))
+    _expect_dims(where, "x", x, (rows, cols))
     _same_gpu(where, q, scale, x)
     st = library().fp8_block_dequantize(_ptr(q), _ptr(scale), rows, cols, _kind(kind), _ptr(x), _stream(stream, q))
     _check(st, "fp8_block_dequantize")
@@ -258,6 +283,12 @@ def fp8_fake_quant_merge(w, lora_b, lora_a, q, scale, wdq=None, stream=None):
     _expect(where, "q", q, _CODES, n * k)
     _expect(where, "scale", scale, _F32, (n // 128) * (k // 128))
     _expect(where, "wdq", wdq, _BF16, n * k)
+    if lora_b.dim() != 2 or tuple(lora_b.shape) != (n, r) or lora_a.dim() != 2 or lora_a.shape[1] != k:
+        raise ValueError(f"{where}: lora_b {tuple(lora_b.shape)} and lora_a {tuple(lora_a.shape)} do not match "
+                         f"w {tuple(w.shape)} (expected ({n}, r) and (r, {k}))")
+    _expect_dims(where, "q", q, (n, k))
+    _expect_dims(where, "scale", scale, (n // 128, k // 128))
+    _expect_dims(where, "wdq", wdq, (n, k))
     _same_gpu(where, w, lora_b, lora_a, q, scale, wdq)
     st = library().fp8_fake_quant_merge(_ptr(w), _ptr(lora_b), _ptr(lora_a), n, k, r, _ptr(q), _ptr(scale),
                                         _ptr(wdq), _stream(stream, w))
@@ -277,6 +308,11 @@ def fp8_block_scaled_gemm(a_q, a_scale, a_kind, b_q, b_scale, b_kind, y, stream=
     sn, sdt = _scale_numel(n, k, b_kind)
     _expect(where, "b_scale", b_scale, sdt, sn)
     _expect(where, "y", y, _OUT, m * n)
+    if b_q.dim() != 2 or b_q.shape[1] != k:
+        raise ValueError(f"{where}: b_q has shape {tuple(b_q.shape)}, expected (n, {k}) to match a_q {tuple(a_q.shape)}")
+    _expect_dims(where, "a_scale", a_scale, _scale_dims(m, k, a_kind))
+    _expect_dims(where, "b_scale", b_scale, _scale_dims(n, k, b_kind))
+    _expect_dims(where, "y", y, (m, n))
     y_type = FP8_OUT_F32 if y.dtype == torch.float32 else FP8_OUT_BF16
     _same_gpu(where, a_q, a_scale, b_q, b_scale, y)
     st = library().fp8_block_scaled_gemm(_ptr(a_q), _ptr(a_scale), _kind(a_kind), _ptr(b_q), _ptr(b_scale),
@@ -293,6 +329,12 @@ def _check_grouped(where, a_q, a_scale, a_kind, a_rows, b_q, b_scale, b_kind, gr
     _expect(where, "b_scale", b_scale, sdt, groups * sn)
     _expect(where, "group_offsets", offsets, _I32, groups + 1)
     _expect(where, "y", y, _OUT, total_m * n)
+    if b_q.dim() != 3 or b_q.shape[2] != k:
+        raise ValueError(f"{where}: b_q has shape {tuple(b_q.shape)}, expected (groups, n, {k}) to match a_q "
+                         f"{tuple(a_q.shape)}")
+    _expect_dims(where, "a_scale", a_scale, _scale_dims(a_rows, k, a_kind))
+    _expect_dims(where, "b_scale", b_scale, (groups,) + _scale_dims(n, k, b_kind))
+    _expect_dims(where, "y", y, (total_m, n))
 
 
 def fp8_grouped_gemm(a_q, a_scale, a_kind, b_q, b_scale, b_kind, group_offsets, y, stream=None):
@@ -382,6 +424,9 @@ def fp8_nvfp4_quantize(x, rows_per_tensor, q, block_scale, global_scale, tensor_
     _expect(where, "global_scale", global_scale, _F32, tensors)
     _expect(where, "tensor_amax", tensor_amax, _F32, tensors)
     _expect(where, "xdq", xdq, _BF16, rows * cols)
+    _expect_dims(where, "q", q, (rows, cols // 2))
+    _expect_dims(where, "block_scale", block_scale, (rows, cols // 16))
+    _expect_dims(where, "xdq", xdq, (rows, cols))
     _same_gpu(where, x, q, block_scale, global_scale, tensor_amax, xdq)
     st = library().fp8_nvfp4_quantize(_ptr(x), rows, cols, rows_per_tensor, _ptr(tensor_amax), 1 if amax_given else 0,
                                       _ptr(q), _ptr(block_scale), _ptr(global_scale), _ptr(xdq), _stream(stream, x))
@@ -399,6 +444,8 @@ def fp8_nvfp4_dequantize(q, block_scale, global_scale, rows_per_tensor, x, strea
     _expect(where, "block_scale", block_scale, _CODES, rows * (cols // 16))
     _expect(where, "global_scale", global_scale, _F32, tensors)
     _expect(where, "x", x, _BF16, rows * cols)
+    _expect_dims(where, "q", q, (rows, cols // 2))
+    _expect_dims(where, "block_scale", block_scale, (rows, cols // 16))
     _same_gpu(where, q, block_scale, global_scale, x)
     st = library().fp8_nvfp4_dequantize(_ptr(q), _ptr(block_scale), _ptr(global_scale), rows, cols, rows_per_tensor,
                                         _ptr(x), _stream(stream, q))

@@ -239,27 +239,37 @@ int fp8_lora_backward_workspace(int64_t m, int64_t n, int64_t k, int64_t r, size
   return FP8_OK;
 }
 
-int fp8_lora_backward(const uint16_t* dy, const uint16_t* x, const uint16_t* lora_b, const uint16_t* lora_a,
-                      int64_t m, int64_t n, int64_t k, int64_t r, void* workspace, size_t workspace_bytes,
-                      void* d_lora_b, void* d_lora_a, int out_type, void* stream) {
+// Arguments of the LoRA backward except the workspace.
+static int lora_args(const uint16_t* dy, const uint16_t* x, const uint16_t* lora_b, const uint16_t* lora_a, int64_t m,
+                     int64_t n, int64_t k, int64_t r, const void* d_lora_b, const void* d_lora_a, int out_type) {
   if (out_type != FP8_OUT_BF16 && out_type != FP8_OUT_F32) return FP8_ERR_INVALID_ARG;
   if (int s = lora_shape(m, n, k, r)) return s;
   if (n == 0 && k == 0) return FP8_OK;
-  if (!workspace || (n > 0 && (!lora_b || !d_lora_b)) || (k > 0 && (!lora_a || !d_lora_a)) ||
+  if ((n > 0 && (!lora_b || !d_lora_b)) || (k > 0 && (!lora_a || !d_lora_a)) ||
       (m > 0 && ((n > 0 && !dy) || (k > 0 && !x))))
     return FP8_ERR_INVALID_ARG;
-  if (workspace_bytes < (size_t)fp8blk::lora_bwd_workspace_bytes(m, n, k, r)) return FP8_ERR_INVALID_ARG;
   const uintptr_t oa = out_type == FP8_OUT_F32 ? 4 : 2;
   if ((dy && !aligned(dy, 16)) || (x && !aligned(x, 16)) || (lora_a && !aligned(lora_a, 16)) ||
-      (lora_b && !aligned(lora_b, 2)) ||
-      !aligned(workspace, 256) || (d_lora_b && !aligned(d_lora_b, oa)) || (d_lora_a && !aligned(d_lora_a, oa)))
+      (lora_b && !aligned(lora_b, 2)) || (d_lora_b && !aligned(d_lora_b, oa)) || (d_lora_a && !aligned(d_lora_a, oa)))
     return FP8_ERR_ALIGN;
+  return FP8_OK;
+}
+
+int fp8_lora_backward(const uint16_t* dy, const uint16_t* x, const uint16_t* lora_b, const uint16_t* lora_a,
+                      int64_t m, int64_t n, int64_t k, int64_t r, void* workspace, size_t workspace_bytes,
+                      void* d_lora_b, void* d_lora_a, int out_type, void* stream) {
+  if (int s = lora_args(dy, x, lora_b, lora_a, m, n, k, r, d_lora_b, d_lora_a, out_type)) return s;
+  if (n == 0 && k == 0) return FP8_OK;
+  if (!workspace) return FP8_ERR_INVALID_ARG;
+  if (workspace_bytes < (size_t)fp8blk::lora_bwd_workspace_bytes(m, n, k, r)) return FP8_ERR_INVALID_ARG;
+  if (!aligned(workspace, 256)) return FP8_ERR_ALIGN;
   DeviceInfo* dev = nullptr;
   if (int s = current_device(&dev)) return s;
   return hip_status(fp8blk::launch_lora_bwd(dy, x, lora_b, lora_a, m, n, k, r, workspace, d_lora_b, d_lora_a,
                                             out_type == FP8_OUT_F32, dev->num_cu,
                                             reinterpret_cast<hipStream_t>(stream)));
 }
+
 
 static int nvfp4_shape(int64_t rows, int64_t cols, int64_t rows_per_tensor) {
   if (rows < 0 || cols < 0 || cols % 16 || !product_at_most(rows, cols, kMaxElements)) return FP8_ERR_SHAPE;
@@ -290,7 +300,8 @@ int fp8_nvfp4_dequantize(const uint8_t* q, const uint8_t* block_scale, const flo
   if (int s = nvfp4_shape(rows, cols, rows_per_tensor)) return s;
   if (rows == 0 || cols == 0) return FP8_OK;
   if (!q || !block_scale || !global_scale || !x) return FP8_ERR_INVALID_ARG;
-  if (!aligned(q, 4) || !aligned(global_scale, 4) || !aligned(x, 16)) return FP8_ERR_ALIGN;
+  // codes are read 8 bytes (one 1x16 block) per lane
+  if (!aligned(q, 8) || !aligned(global_scale, 4) || !aligned(x, 16)) return FP8_ERR_ALIGN;
   DeviceInfo* dev = nullptr;
   if (int s = current_device(&dev)) return s;
   return hip_status(fp8blk::launch_nvfp4_dequant(q, block_scale, global_scale, rows, cols, rows_per_tensor, x,

@@ -306,6 +306,7 @@ int fp8_lora_backward(const uint16_t* dy, const uint16_t* x, const uint16_t* lor
  * (host pointer).  Same shape checks and status codes as the call itself. */
 int fp8_lora_backward_workspace(int64_t m, int64_t n, int64_t k, int64_t r, size_t* bytes);
 
+
 /*
  * fp8_nvfp4_quantize -- NVFP4 prequantization: packed FP4 values with FP8
  * block scales.
@@ -342,7 +343,7 @@ int fp8_nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ro
  *   x = RN_bf16(RN32(e2m1(code) * RN32(e4m3(S) * g))), the value
  * fp8_nvfp4_quantize writes to xdq.  Defined by: [prequant] "Formats"
  * (serving loads the packed weights); arguments and shape as there (q
- * 4-byte aligned here).
+ * 8-byte aligned: one 1x16 block of codes is read as 8 bytes).
  */
 int fp8_nvfp4_dequantize(const uint8_t* q, const uint8_t* block_scale, const float* global_scale,
                          int64_t rows, int64_t cols, int64_t rows_per_tensor, uint16_t* x, void* stream);

@@ -218,9 +218,10 @@ def test_python_binding_rejects_host_tensors(lib):
         fb.fp8_block_quantize(x, "1x32", "ceil", q, s)
     w = torch.zeros((128, 128), dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="on a GPU"):
-        fb.fp8_block_scaled_gemm(q, torch.zeros((4, 1), dtype=torch.float32), "1x128",
-                                 torch.zeros((128, 64), dtype=torch.uint8), torch.zeros((1, 1), dtype=torch.float32),
-                                 "128x128", torch.zeros((4, 128), dtype=torch.bfloat16))
+        fb.fp8_block_scaled_gemm(torch.zeros((4, 128), dtype=torch.uint8), torch.zeros((4, 1), dtype=torch.float32),
+                                 "1x128", torch.zeros((128, 128), dtype=torch.uint8),
+                                 torch.zeros((1, 1), dtype=torch.float32), "128x128",
+                                 torch.zeros((4, 128), dtype=torch.bfloat16))
     with pytest.raises(ValueError, match="on a GPU"):
         fb.fp8_fake_quant_merge(w, torch.zeros((128, 4), dtype=torch.bfloat16),
                                 torch.zeros((4, 128), dtype=torch.bfloat16), torch.zeros((128, 128), dtype=torch.uint8),
@@ -279,6 +280,48 @@ def test_python_binding_checks_dtypes_and_sizes(lib):
                              torch.zeros((4, 255), dtype=bf))
 
 
+def test_python_binding_checks_shapes(lib):
+    """Operands whose shapes disagree with the sizes the library derives
+    (a wider B row, LoRA factors of another rank or width, a transposed
+    scale array) are refused: the kernels would read them with the wrong
+    strides."""
+    import torch
+    bf, u8, f32 = torch.bfloat16, torch.uint8, torch.float32
+    a = torch.zeros((8, 256), dtype=u8)
+    sa = torch.zeros((8, 2), dtype=f32)
+    b = torch.zeros((128, 256), dtype=u8)
+    sb = torch.zeros((1, 2), dtype=f32)
+    y = torch.zeros((8, 128), dtype=bf)
+    with pytest.raises(ValueError, match="b_q has shape"):
+        fb.fp8_block_scaled_gemm(a, sa, "1x128", torch.zeros((128, 384), dtype=u8), sb, "128x128", y)
+    with pytest.raises(ValueError, match="a_scale has shape"):
+        fb.fp8_block_scaled_gemm(a, torch.zeros((2, 8), dtype=f32), "1x128", b, sb, "128x128", y)
+    with pytest.raises(ValueError, match="b_scale has shape"):
+        fb.fp8_block_scaled_gemm(a, sa, "1x128", b, torch.zeros((2, 1), dtype=f32), "128x128", y)
+    with pytest.raises(ValueError, match="y has shape"):
+        fb.fp8_block_scaled_gemm(a, sa, "1x128", b, sb, "128x128", torch.zeros((16, 64), dtype=bf))
+    bg = torch.zeros((3, 128, 256), dtype=u8)
+    sbg = torch.zeros((3, 128, 8), dtype=u8)
+    offs = torch.zeros((4,), dtype=torch.int32)
+    with pytest.raises(ValueError, match="b_q has shape"):
+        fb.fp8_grouped_gemm(a, sa, "1x128", torch.zeros((3, 128, 384), dtype=u8), sbg, "1x32", offs, y)
+    with pytest.raises(ValueError, match="b_scale has shape"):
+        fb.fp8_grouped_gemm(a, sa, "1x128", bg, torch.zeros((3, 8, 128), dtype=u8), "1x32", offs, y)
+    w = torch.zeros((128, 256), dtype=bf)
+    q = torch.zeros((128, 256), dtype=u8)
+    s = torch.zeros((1, 2), dtype=f32)
+    with pytest.raises(ValueError, match="lora_b"):
+        fb.fp8_fake_quant_merge(w, torch.zeros((128, 8), dtype=bf), torch.zeros((4, 256), dtype=bf), q, s)
+    with pytest.raises(ValueError, match="lora_b"):
+        fb.fp8_fake_quant_merge(w, torch.zeros((128, 4), dtype=bf), torch.zeros((4, 512), dtype=bf), q, s)
+    with pytest.raises(ValueError, match="q has shape"):
+        fb.fp8_block_quantize(torch.zeros((4, 256), dtype=bf), "1x128", "ceil", torch.zeros((8, 128), dtype=u8),
+                              torch.zeros((4, 2), dtype=f32))
+    with pytest.raises(ValueError, match="block_scale has shape"):
+        fb.fp8_nvfp4_dequantize(torch.zeros((4, 16), dtype=u8), torch.zeros((2, 4), dtype=u8),
+                                torch.zeros((1,), dtype=f32), 4, torch.zeros((4, 32), dtype=bf))
+
+
 def test_routed_expert_name_rule():
     yes = ["model.layers.3.mlp.experts.0.gate_proj.weight",
            "model.layers.60.mlp.experts.255.up_proj.weight",
@@ -324,3 +367,4 @@ def test_nvfp4_validation(lib):
     assert d(None, None, None, 0, 32, 1, None, None) == OK
     assert d(A16, None, A16, 4, 32, 4, A16, None) == INVALID
     assert d(A16, A16, A16, 4, 32, 4, A16 + 8, None) == ALIGN
+    assert d(A16 + 4, A16, A16, 4, 32, 4, A16, None) == ALIGN      # codes: 8 B (one 1x16 block per lane)
