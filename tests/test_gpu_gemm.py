@@ -15,7 +15,7 @@ import block_scaled_fp8_amax_amd as fb
 from oracle import codec, gemm, quant
 from tests.gpu_helpers import bf16_from_bits, to_np_u8
 from workloads import (bf16_bits, dense_projection, expert_factors, expert_weights, moe_tokens, mx_small,
-                       qat_forward, zipf_routing)
+                       normal_bf16, qat_forward, zipf_routing)
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-3
@@ -42,10 +42,16 @@ def _check_gemm(aq, sa, ka, bq, sb, kb, rows=None, label=""):
         y32n, y16n = y32.cpu().numpy()[rows], bf16_bits(y16)[rows]
     else:
         y32n, y16n = y32.cpu().numpy(), bf16_bits(y16)
-    ref = gemm.gemm_ref32(aqn, san, ka, bq.cpu().numpy(), sb.cpu().numpy(), kb)
+    bqn, sbn = bq.cpu().numpy(), sb.cpu().numpy()
+    ref = gemm.gemm_ref32(aqn, san, ka, bqn, sbn, kb)
+    ref64 = gemm.gemm_ref64(aqn, san, ka, bqn, sbn, kb)
     err = gemm.normwise_rel_err(y32n, ref)
-    print(f"[gemm] {label} normwise rel err {err:.3e}", flush=True)
+    err64 = gemm.normwise_rel_err(y32n, ref64)
+    gap = gemm.normwise_rel_err(ref, ref64)
+    print(f"[gemm] {label} normwise rel err {err:.3e} (vs fp64 {err64:.3e}; fp32 reference vs fp64 {gap:.3e})",
+          flush=True)
     assert err <= TOL
+    assert err64 <= TOL
     assert np.array_equal(y16n, codec.f32_to_bf16(y32n))
     yb = codec.bf16_to_f32(y16n).astype(np.float64)
     bound = 2.0 ** -8 * np.abs(ref) + TOL * np.abs(ref).max()
@@ -99,7 +105,7 @@ def test_dense_projection_full():
     d = dense_projection("cuda")
     aq, sa = _q(d["x"], "1x128")
     bq, sb = _q(d["w"], "128x128")
-    rows = np.sort(np.random.default_rng(3).choice(4096, 512, replace=False))
+    rows = np.sort(np.random.default_rng(3).choice(4096, 256, replace=False))
     _check_gemm(aq, sa, "1x128", bq, sb, "128x128", rows=rows, label="dense projection 4096x2048x7168")
 
 
@@ -107,7 +113,7 @@ def test_qat_gemm_full_sampled():
     d = qat_forward("cuda")
     aq, sa = _q(d["x"], "1x128")
     wq, ws = fb.fake_quant_merge(d["w"], d["lora_b"], d["lora_a"])
-    rows = np.sort(np.random.default_rng(4).choice(8192, 256, replace=False))
+    rows = np.sort(np.random.default_rng(4).choice(8192, 96, replace=False))
     _check_gemm(aq, sa, "1x128", wq.view(torch.uint8), ws, "128x128", rows=rows,
                 label="QAT 8192x7168x7168")
 
@@ -233,17 +239,60 @@ def test_grouped_moe_full():
     order = np.argsort(sizes)
     groups = sorted(set([int(order[0]), int(order[-1]), int(order[len(order) // 2])] +
                         list(np.random.default_rng(5).choice(256, 5, replace=False))))
-    rng = np.random.default_rng(6)
+    _check_sampled_groups(y, y32, aq, sa, bq, sb, offn, groups, np.random.default_rng(6), "gate||up")
+
+
+def _check_sampled_groups(y, y32, aq, sa, bq, sb, offn, groups, rng, label, per_group=64):
+    """Sampled rows of the given groups against the oracle: the k-ordered
+    fp32 reference (the bound), the fp64 product, and the gap between the
+    two references; bf16 output equal to RN_bf16 of the fp32 output."""
     for g in groups:
         lo, hi = int(offn[g]), int(offn[g + 1])
-        rows = np.arange(lo, hi) if hi - lo <= 256 else np.sort(rng.choice(np.arange(lo, hi), 256, replace=False))
-        ref = gemm.gemm_ref32(aq[rows].cpu().numpy(), sa[rows].cpu().numpy(), "1x128",
-                              bq[g].cpu().numpy(), sb[g].cpu().numpy(), "1x32")
+        rows = np.arange(lo, hi) if hi - lo <= per_group else np.sort(rng.choice(np.arange(lo, hi), per_group,
+                                                                                 replace=False))
+        an, san = aq[rows].cpu().numpy(), sa[rows].cpu().numpy()
+        bn, sbn = bq[g].cpu().numpy(), sb[g].cpu().numpy()
+        ref = gemm.gemm_ref32(an, san, "1x128", bn, sbn, "1x32")
+        ref64 = gemm.gemm_ref64(an, san, "1x128", bn, sbn, "1x32")
         got = y32[rows].cpu().numpy()
         err = gemm.normwise_rel_err(got, ref)
-        print(f"[grouped] group {g} rows {hi - lo} err {err:.3e}", flush=True)
+        err64 = gemm.normwise_rel_err(got, ref64)
+        gap = gemm.normwise_rel_err(ref, ref64)
+        print(f"[grouped] {label} group {g} rows {hi - lo} err {err:.3e} (vs fp64 {err64:.3e}; fp32 reference vs "
+              f"fp64 {gap:.3e})", flush=True)
         assert err <= TOL
+        assert err64 <= TOL
         assert np.array_equal(bf16_bits(y[rows]), codec.f32_to_bf16(got))
+
+
+def test_grouped_moe_down_full():
+    """The experts' down projection at its full shape: 131072 routed rows of
+    the intermediate activations (K 2048, quantized per row in 1x128 tiles)
+    against 256 MXFP8 down weights (N 7168, K 2048); the largest, smallest
+    and median groups and 5 random ones are checked on sampled rows."""
+    tok, off = zipf_routing()
+    total = int(off[-1])
+    h = normal_bf16((total, 2048), 1.0, 510, "cuda")
+    hq, hs = _q(h, "1x128")
+    del h
+    fac = expert_factors()
+    bq = torch.empty((256, 7168, 2048), dtype=torch.uint8, device="cuda")
+    sb = torch.empty((256, 7168, 64), dtype=torch.uint8, device="cuda")
+    for e in range(256):
+        _, _, down = expert_weights(e, "cuda", fac)
+        wq, ws = _q(down, "1x32")
+        bq[e].copy_(wq)
+        sb[e].copy_(ws)
+    offt = off.cuda()
+    print("[grouped] MoE down projection 131072x7168x2048, 256 groups", flush=True)
+    y = _grouped(hq, hs, bq, sb, "1x32", offt, torch.bfloat16)
+    y32 = _grouped(hq, hs, bq, sb, "1x32", offt, torch.float32)
+    offn = off.numpy()
+    sizes = offn[1:] - offn[:-1]
+    order = np.argsort(sizes)
+    groups = sorted(set([int(order[0]), int(order[-1]), int(order[len(order) // 2])] +
+                        list(np.random.default_rng(7).choice(256, 5, replace=False))))
+    _check_sampled_groups(y, y32, hq, hs, bq, sb, offn, groups, np.random.default_rng(8), "down")
 
 
 # ------------------------------------------------------------ gathered rows

@@ -2,7 +2,8 @@
 
 Codes, scales and fake-quant outputs must equal the oracle's bytes.  Cases:
 shapes spanning several blocks and ragged row counts, every block kind and
-E8M0 rule, an exhaustive-per-mantissa domain sweep of (x, amax) pairs, the
+E8M0 rule, an exhaustive domain sweep of (x, amax) pairs (every pair for
+the fp32 scales, every pair under every E8M0 exponent), the
 degenerate blocks (all zero, signed zeros, subnormal and huge amax), the
 full-size activation/weight shapes of the dense and QAT projections, the
 MXFP8 prequantization of a whole MoE layer's routed experts, and
@@ -114,16 +115,69 @@ def test_domain_fp32_scale():
     _check(blocks, "1x128", "ceil")
 
 
+def _domain_chunks(target=8 << 20):
+    """Consecutive ranges [a0, a1) of positive finite bf16 amax patterns
+    (0x0001 .. 0x7F7F) whose blocks hold about ``target`` elements each."""
+    sizes = 2 * (np.arange(1, 0x7F80, dtype=np.int64) + 1)        # elements of amax ab: 2 (ab + 1)
+    out, a0, acc = [], 1, 0
+    for ab, sz in zip(range(1, 0x7F80), sizes):
+        acc += int(sz)
+        if acc >= target:
+            out.append((a0, ab + 1))
+            a0, acc = ab + 1, 0
+    if a0 < 0x7F80:
+        out.append((a0, 0x7F80))
+    return out
+
+
+def test_domain_fp32_scale_exhaustive():
+    """Every pair (x, amax) of finite bf16 values with |x| <= amax, amax > 0:
+    each of the 32639 positive finite amax patterns heads 1x128 blocks whose
+    other 127 elements run through every bf16 magnitude up to amax, both
+    signs (about 1.07e9 elements).  Codes and scales equal the oracle's; the
+    oracle runs chunk by chunk on the host's cores (numpy releases the GIL)
+    while the GPU quantizes the same chunks."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+    chunks = _domain_chunks()
+    threads = max(1, min(16, os.cpu_count() or 1))
+
+    def oracle_chunk(c):
+        a0, a1 = c
+        blocks = _domain_blocks(np.arange(a0, a1, dtype=np.uint32), 128)
+        oq, os_, _ = quant.quantize(blocks, "1x128")
+        return blocks, oq, os_
+
+    print(f"[quantize] exhaustive (x, amax) fp32-scale sweep: {len(chunks)} chunks on {threads} host threads",
+          flush=True)
+    elems = 0
+    with ThreadPoolExecutor(threads) as ex:
+        pending = [ex.submit(oracle_chunk, c) for c in chunks[:2 * threads]]
+        nxt = len(pending)
+        for i in range(len(chunks)):
+            blocks, oq, os_ = pending[i].result()
+            pending[i] = None
+            if nxt < len(chunks):
+                pending.append(ex.submit(oracle_chunk, chunks[nxt]))
+                nxt += 1
+            q, s, _ = run_quantize(bf16_from_bits(blocks), "1x128", "ceil", dequant=False)
+            assert_bytes_equal(q, oq, f"exhaustive chunk {chunks[i]} codes")
+            assert_bytes_equal(s, os_, f"exhaustive chunk {chunks[i]} scales")
+            elems += blocks.size
+    print(f"[quantize] exhaustive sweep: {elems} elements equal", flush=True)
+    assert elems >= 32639 * 32640
+
+
 def test_domain_e8m0_every_exponent():
     """For every E8M0 code: a block whose amax sets that code, with every bf16
-    magnitude up to amax (subsampled 1 in 3) and both signs."""
+    magnitude up to amax and both signs."""
     amax = []
     for e in range(1, 255):
         amax.append((e << 7) | 0x60)      # 1.75 * 2^(e-127): ceil code e-8
         amax.append((e << 7) | 0x61)
     blocks = []
     for ab in amax:
-        xs = np.arange(0, ab + 1, 3, dtype=np.uint32).astype(np.uint16)
+        xs = np.arange(0, ab + 1, dtype=np.uint32).astype(np.uint16)
         xs = np.concatenate([xs, xs | 0x8000])
         pad = (-len(xs)) % 31
         xs = np.concatenate([xs, np.zeros(pad, np.uint16)]).reshape(-1, 31)
