@@ -1,18 +1,19 @@
 """Benchmark of the block-scaled FP8 hot path on one MI355X.
 
 One step = one pass of the path over one batch of synthetic input.  The
-default workload is the DeepSeek-V3-shaped dense projection (weights bf16
-2048x7168 quantized in 128x128 blocks, activations bf16 4096x7168 quantized
-per token in 1x128 tiles, block-scaled FP8 GEMM M=4096 N=2048 K=7168 with
-per-128-K promotion, bf16 out):
-    fp8_block_quantize_batch([W 128x128, X 1x128])   (one launch)
-    -> fp8_block_scaled_gemm(A = X codes, B = W codes)
-Inputs are resident in HBM before timing starts; several input sets rotate
-so that no step finds its inputs in the 256 MB Infinity Cache.
+default workload is the largest one-GPU configuration, the grouped MoE
+expert GEMM: 16384 tokens of hidden 7168 quantized per token in 1x128 tiles,
+then the gate||up projection of their top-8 routed copies (Zipf(1.1) over
+256 experts, sum M 131072, N 4096, K 7168) against MXFP8 expert weights,
+fp32 accumulation, bf16 out:
+    fp8_block_quantize(X 16384x7168, 1x128)
+    -> fp8_grouped_gemm(A = routed rows, B = 256 experts' gate||up codes)
+(the routed rows are gathered into expert order once, outside the timed
+region).  Inputs are resident in HBM before timing starts.
 
 Prints one JSON line.  ``value`` is the step's throughput in GEMM TFLOP/s
-(2*M*N*K per step over the measured step time).  ``roofline`` describes the
-dominant kernel (the GEMM): its average duration comes from HIP events on
+(2*sum(M)*N*K per step over the measured step time).  ``roofline``
+describes the dominant kernel (the GEMM): its average duration comes from HIP events on
 the stream the kernel runs on, around a back-to-back loop of it run right
 after the timed region (its time between per-launch events inside whole
 steps, from the untimed pass below, is reported beside it).  ``components`` gives every kernel's own time, GB/s and
@@ -20,11 +21,13 @@ roofline fraction from a separate, untimed pass with events around each
 launch.
 
 Other workloads (``--config``) print the same kind of line for their own
-path: mx (MXFP8 quantize of W 256x512 and X 64x512, MX x MX GEMM), qat
+path: dense (the DeepSeek-V3-shaped dense projection: W 2048x7168 quantized
+in 128x128 blocks and X 4096x7168 in 1x128 tiles in one batched launch,
+GEMM 4096x2048x7168 with per-128-K promotion), mx (MXFP8 quantize of W
+256x512 and X 64x512, MX x MX GEMM), qat
 (LoRA merge + 128x128 fake-quant of W 7168x7168, 1x128 fake-quant of X
 8192x7168, GEMM 8192x7168x7168), prequant (MXFP8 quantization of one MoE
-layer's 256 routed experts), moe (per-token quantize of 16384x7168 and
-the grouped gate||up expert GEMM over Zipf(1.1) top-8 routing), moe_gather
+layer's 256 routed experts), moe (the default, above), moe_gather
 (the same with the routed rows read through row_index), moe_down (the
 experts' down projection, K 2048, N 7168), dequant (the MXFP8 MoE layer
 back to bf16), qat_backward (the QAT backward for the LoRA factors of the
@@ -528,14 +531,39 @@ def recorded_traffic(config):
 # ------------------------------------------------------------- cpu baseline
 
 def _oracle_threads():
-    threads = torch.get_num_threads()
+    """Threads the oracle runs on: its arithmetic is numpy elementwise work
+    (one thread), and any BLAS call it makes is pinned to one thread while
+    the baseline is timed (``_one_thread``)."""
+    return 1
+
+
+class _one_thread:
+    """Limit BLAS / OpenMP pools to one thread while the oracle is timed."""
+
+    def __enter__(self):
+        self._ctl = None
+        try:
+            import threadpoolctl
+            self._ctl = threadpoolctl.threadpool_limits(1)
+        except Exception:  # noqa: BLE001
+            pass
+        return self
+
+    def __exit__(self, *exc):
+        if self._ctl is not None:
+            self._ctl.restore_original_limits()
+        return False
+
+
+def _cpu_model():
     try:
-        import threadpoolctl
-        info = threadpoolctl.threadpool_info()
-        threads = max([i.get("num_threads", 1) for i in info] + [1])
-    except Exception:  # noqa: BLE001
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
         pass
-    return threads
+    return "unknown"
 
 
 def cpu_baseline_dense(sample_rows=256):
@@ -621,8 +649,8 @@ def cpu_baseline_quant_expert(dequant=False):
             "sample": f"{what} of expert 0's gate projection 2048x7168 (1x32, E8M0); {secs:.2f} s"}
 
 
-def cpu_baseline_grouped(n=4096, k=7168, rows=256, down=False):
-    """The oracle on one routed slice of the grouped step: quantize 256
+def cpu_baseline_grouped(n=4096, k=7168, rows=1024, down=False):
+    """The oracle on one routed slice of the grouped step: quantize ``rows``
     activation rows (1x128) and their GEMM against one expert's weights."""
     import workloads
     from oracle import gemm as ogemm, quant as oquant
@@ -804,13 +832,18 @@ def run(args):
         "ms_per_step": ms_per_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": wl.dtype,
-        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) activations with 1% channels x50)",
+        "data": "synthetic, seeded: N(0,0.02) weights (routed experts scaled log-uniform in [0.5,2]), N(0,1) "
+                "activations with 1% of channels x50, Zipf(1.1) top-8 routing over 256 experts",
         "config": wl.cfg,
         "components": components,
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = CPU_BASELINES[args.config]()
+        with _one_thread():
+            cb = CPU_BASELINES[args.config]()
+        cb["cpu_model"] = _cpu_model()
+        cb["host_cpus"] = os.cpu_count()
+        out["cpu_baseline"] = cb
     print(json.dumps(out), flush=True)
 
 
@@ -830,9 +863,9 @@ def copy_calibration(args):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="dense", choices=sorted(WORKLOADS))
+    ap.add_argument("--config", default="moe", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 1 GiB device copies (counter calibration under rocprofv3)")
