@@ -21,6 +21,7 @@ __all__ = [
     "Fp8Error", "library", "library_path",
     "fp8_block_quantize", "fp8_block_quantize_batch", "fp8_block_dequantize", "fp8_fake_quant_merge", "fp8_block_scaled_gemm",
     "fp8_grouped_gemm", "fp8_grouped_gemm_gather", "fp8_lora_backward", "fp8_lora_backward_workspace",
+    "fp8_lora_backward_noalloc", "NOALLOC_SCRATCH_BYTES",
     "fp8_nvfp4_quantize", "fp8_nvfp4_dequantize",
     "fp8_status_string", "fp8_abi_version",
     "quantize", "dequantize", "fake_quant_merge", "block_scaled_gemm", "grouped_gemm", "lora_backward", "nvfp4_quantize", "nvfp4_dequantize",
@@ -32,7 +33,8 @@ FP8_OK = 0
 FP8_BLOCK_1x32_E8M0, FP8_BLOCK_1x128_F32, FP8_BLOCK_128x128_F32 = 0, 1, 2
 FP8_E8M0_CEIL, FP8_E8M0_FLOOR = 0, 1
 FP8_OUT_BF16, FP8_OUT_F32 = 0, 1
-ABI_VERSION = 5
+ABI_VERSION = 6
+NOALLOC_SCRATCH_BYTES = 40 << 20    # fixed scratch of fp8_lora_backward_noalloc (per device)
 
 _KIND_NAMES = {"1x32": FP8_BLOCK_1x32_E8M0, "1x128": FP8_BLOCK_1x128_F32, "128x128": FP8_BLOCK_128x128_F32}
 _RULE_NAMES = {"ceil": FP8_E8M0_CEIL, "floor": FP8_E8M0_FLOOR}
@@ -79,6 +81,8 @@ def library():
         lib.fp8_grouped_gemm_gather.restype = ci
         lib.fp8_lora_backward.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, vp, ctypes.c_size_t, vp, vp, ci, vp]
         lib.fp8_lora_backward.restype = ci
+        lib.fp8_lora_backward_noalloc.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, vp, vp, ci, vp]
+        lib.fp8_lora_backward_noalloc.restype = ci
         lib.fp8_lora_backward_workspace.argtypes = [i64, i64, i64, i64, ctypes.POINTER(ctypes.c_size_t)]
         lib.fp8_lora_backward_workspace.restype = ci
         lib.fp8_nvfp4_quantize.argtypes = [vp, i64, i64, i64, vp, ci, vp, vp, vp, vp, vp]
@@ -406,6 +410,32 @@ def fp8_lora_backward(dy, x, lora_b, lora_a, workspace, d_lora_b, d_lora_a, stre
                                      workspace.numel() * workspace.element_size(), _ptr(d_lora_b), _ptr(d_lora_a),
                                      out_type, _stream(stream, dy))
     _check(st, "fp8_lora_backward")
+
+
+def fp8_lora_backward_noalloc(dy, x, lora_b, lora_a, d_lora_b, d_lora_a, stream=None):
+    """fp8_lora_backward without a workspace: the library's fixed per-device
+    scratch (NOALLOC_SCRATCH_BYTES) stands in for it and nothing is
+    allocated.  Calls that may overlap on one device must be serialized by
+    the caller; problems whose workspace exceeds the scratch raise
+    (status FP8_ERR_TOO_LARGE)."""
+    _contig(dy, x, lora_b, lora_a, d_lora_b, d_lora_a)
+    m, n = dy.shape
+    k = x.shape[1]
+    r = lora_a.shape[0]
+    if x.shape[0] != m or lora_b.shape != (n, r) or lora_a.shape != (r, k):
+        raise ValueError("fp8_lora_backward_noalloc: inconsistent shapes")
+    if d_lora_b.dtype != d_lora_a.dtype:
+        raise ValueError("fp8_lora_backward_noalloc: both gradients must have one dtype")
+    where = "fp8_lora_backward_noalloc"
+    for name, t in (("dy", dy), ("x", x), ("lora_b", lora_b), ("lora_a", lora_a)):
+        _expect(where, name, t, _BF16, 0)
+    _expect(where, "d_lora_b", d_lora_b, _OUT, n * r)
+    _expect(where, "d_lora_a", d_lora_a, _OUT, r * k)
+    out_type = FP8_OUT_F32 if d_lora_b.dtype == torch.float32 else FP8_OUT_BF16
+    _same_gpu(where, dy, x, lora_b, lora_a, d_lora_b, d_lora_a)
+    st = library().fp8_lora_backward_noalloc(_ptr(dy), _ptr(x), _ptr(lora_b), _ptr(lora_a), m, n, k, r,
+                                             _ptr(d_lora_b), _ptr(d_lora_a), out_type, _stream(stream, dy))
+    _check(st, where)
 
 
 def fp8_nvfp4_quantize(x, rows_per_tensor, q, block_scale, global_scale, tensor_amax, xdq=None, amax_given=False,

@@ -48,6 +48,9 @@ bool product_at_most(int64_t a, int64_t b, int64_t lim) { return b == 0 || a <= 
 
 // Element counts beyond 2^60 are rejected before any size arithmetic.
 constexpr int64_t kMaxElements = int64_t(1) << 60;
+static_assert(FP8BLK_NOALLOC_SCRATCH_BYTES == (unsigned long long)fp8blk::kLoraScratchBytes,
+              "header and library agree on the no-allocation scratch size");
+
 // GEMM reductions: per-tile A/B offsets are 32-bit (256 rows x K bytes).
 constexpr int64_t kMaxGemmK = int64_t(1) << 24;
 
@@ -73,6 +76,7 @@ const char* fp8_status_string(int s) {
     case FP8_ERR_ALIGN: return "pointer not aligned as required";
     case FP8_ERR_UNSUPPORTED: return "unsupported block-kind combination or device (gfx950 required)";
     case FP8_ERR_HIP: return "HIP runtime error";
+    case FP8_ERR_TOO_LARGE: return "problem larger than the library's fixed no-allocation scratch buffer";
     default: return "unknown status";
   }
 }
@@ -239,7 +243,7 @@ int fp8_lora_backward_workspace(int64_t m, int64_t n, int64_t k, int64_t r, size
   return FP8_OK;
 }
 
-// Arguments of the LoRA backward except the workspace.
+// Arguments of both LoRA backward entry points except the workspace.
 static int lora_args(const uint16_t* dy, const uint16_t* x, const uint16_t* lora_b, const uint16_t* lora_a, int64_t m,
                      int64_t n, int64_t k, int64_t r, const void* d_lora_b, const void* d_lora_a, int out_type) {
   if (out_type != FP8_OUT_BF16 && out_type != FP8_OUT_F32) return FP8_ERR_INVALID_ARG;
@@ -270,6 +274,22 @@ int fp8_lora_backward(const uint16_t* dy, const uint16_t* x, const uint16_t* lor
                                             reinterpret_cast<hipStream_t>(stream)));
 }
 
+int fp8_lora_backward_noalloc(const uint16_t* dy, const uint16_t* x, const uint16_t* lora_b, const uint16_t* lora_a,
+                              int64_t m, int64_t n, int64_t k, int64_t r, void* d_lora_b, void* d_lora_a,
+                              int out_type, void* stream) {
+  if (int s = lora_args(dy, x, lora_b, lora_a, m, n, k, r, d_lora_b, d_lora_a, out_type)) return s;
+  if (n == 0 && k == 0) return FP8_OK;
+  if (fp8blk::lora_bwd_workspace_bytes(m, n, k, r) > fp8blk::kLoraScratchBytes) return FP8_ERR_TOO_LARGE;
+  DeviceInfo* dev = nullptr;
+  if (int s = current_device(&dev)) return s;
+  int id = 0;
+  if (hipGetDevice(&id) != hipSuccess) return FP8_ERR_HIP;
+  void* ws = nullptr;
+  if (fp8blk::lora_bwd_scratch(id, &ws) != hipSuccess) return FP8_ERR_HIP;
+  return hip_status(fp8blk::launch_lora_bwd(dy, x, lora_b, lora_a, m, n, k, r, ws, d_lora_b, d_lora_a,
+                                            out_type == FP8_OUT_F32, dev->num_cu,
+                                            reinterpret_cast<hipStream_t>(stream)));
+}
 
 static int nvfp4_shape(int64_t rows, int64_t cols, int64_t rows_per_tensor) {
   if (rows < 0 || cols < 0 || cols % 16 || !product_at_most(rows, cols, kMaxElements)) return FP8_ERR_SHAPE;

@@ -50,6 +50,14 @@ hipError_t launch_grouped_gemm(const uint8_t* a, const void* sa, int a_kind, con
                                hipStream_t stream);
 
 int64_t lora_bwd_workspace_bytes(int64_t m, int64_t n, int64_t k, int64_t r);
+// Fixed scratch of the no-allocation LoRA backward (one array per device):
+// 40 MiB holds the workspace of 8192 tokens at hidden sizes 7168 and rank
+// 64 (36.4 MiB).
+constexpr int64_t kLoraScratchBytes = int64_t(40) << 20;
+constexpr int kMaxScratchDevices = 64;
+// The device address of `dev`'s scratch array (looked up once per device,
+// with `dev` current).
+hipError_t lora_bwd_scratch(int dev, void** ptr);
 hipError_t launch_lora_bwd(const uint16_t* dy, const uint16_t* x, const uint16_t* lb, const uint16_t* la, int64_t m,
                            int64_t n, int64_t k, int64_t r, void* workspace, void* d_b, void* d_a, bool out_f32,
                            int num_cu, hipStream_t stream);

@@ -33,10 +33,38 @@
 // index, 8 per lane group; which hidden or token index each (lane group,
 // element) pair stands for is free as long as both operands agree, and both
 // operands are loaded with the same assignment below.
+#include <mutex>
+
 #include "device.h"
 #include "launch.h"
 
+// Scratch of fp8_lora_backward_noalloc: the workspace of the kernels below
+// in a fixed device array, for callers that cannot allocate.  Each GPU the
+// library runs on holds its own copy until the process ends.  Host code
+// never uses the name itself (on the host it is a stand-in, not a device
+// address): lora_bwd_scratch looks up the address once per device.
+static __device__ __align__(256) uint8_t scratch[fp8blk::kLoraScratchBytes];
+
 namespace fp8blk {
+
+namespace {
+struct ScratchSlot {
+  std::once_flag once;
+  hipError_t err = hipSuccess;
+  void* ptr = nullptr;
+};
+ScratchSlot g_scratch[kMaxScratchDevices];
+}  // namespace
+
+hipError_t lora_bwd_scratch(int dev, void** ptr) {
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  ScratchSlot& s = g_scratch[dev];
+  // runs with `dev` current (the caller's device), once per device
+  std::call_once(s.once, [&s] { s.err = hipGetSymbolAddress(&s.ptr, HIP_SYMBOL(scratch)); });
+  if (s.err != hipSuccess) return s.err;
+  *ptr = s.ptr;
+  return hipSuccess;
+}
 
 namespace {
 

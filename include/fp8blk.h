@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define FP8BLK_ABI_VERSION 5
+#define FP8BLK_ABI_VERSION 6
 
 typedef enum {
   FP8_OK = 0,
@@ -55,7 +55,8 @@ typedef enum {
   FP8_ERR_SHAPE = 2,       /* negative or non-divisible dimension            */
   FP8_ERR_ALIGN = 3,       /* pointer not aligned as documented              */
   FP8_ERR_UNSUPPORTED = 4, /* block-kind combination or device not handled   */
-  FP8_ERR_HIP = 5          /* the HIP runtime reported an error              */
+  FP8_ERR_HIP = 5,         /* the HIP runtime reported an error              */
+  FP8_ERR_TOO_LARGE = 6    /* needs more than the fixed no-allocation scratch */
 } fp8_status;
 
 /* Block geometry and scale type ([DSV3-Blog5] block-wise quantization;
@@ -306,6 +307,29 @@ int fp8_lora_backward(const uint16_t* dy, const uint16_t* x, const uint16_t* lor
  * (host pointer).  Same shape checks and status codes as the call itself. */
 int fp8_lora_backward_workspace(int64_t m, int64_t n, int64_t k, int64_t r, size_t* bytes);
 
+/*
+ * fp8_lora_backward_noalloc -- fp8_lora_backward without a workspace
+ * argument and without any allocation, for callers that cannot allocate
+ * device memory (code under stream or graph capture, tight serving loops,
+ * harnesses that forbid allocation).
+ *
+ * Same computation, arguments (minus workspace / workspace_bytes), shape
+ * rules, alignment and results as fp8_lora_backward: the output bytes are
+ * identical.  The workspace is a fixed array of FP8BLK_NOALLOC_SCRATCH_BYTES
+ * bytes per device, held by the library from first use until the process
+ * ends; its contents on entry do not matter.  Problems whose workspace
+ * (fp8_lora_backward_workspace) exceeds it return FP8_ERR_TOO_LARGE and
+ * enqueue nothing (40 MiB: 8192 tokens at n = k = 7168 fit up to rank 64).
+ * Every call on one device shares that device's array: calls that may
+ * overlap on one device (other streams, other host threads) race and must
+ * be serialized by the caller.  The array's address is looked up on the
+ * first call on each device, with that device current; nothing is
+ * allocated then either.
+ */
+#define FP8BLK_NOALLOC_SCRATCH_BYTES (40ull << 20)
+int fp8_lora_backward_noalloc(const uint16_t* dy, const uint16_t* x, const uint16_t* lora_b,
+                              const uint16_t* lora_a, int64_t m, int64_t n, int64_t k, int64_t r,
+                              void* d_lora_b, void* d_lora_a, int out_type, void* stream);
 
 /*
  * fp8_nvfp4_quantize -- NVFP4 prequantization: packed FP4 values with FP8

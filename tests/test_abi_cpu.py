@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == {"fp8_block_quantize", "fp8_block_quantize_batch", "fp8_block_dequantize",
                           "fp8_fake_quant_merge",
                           "fp8_block_scaled_gemm", "fp8_grouped_gemm", "fp8_grouped_gemm_gather",
-                          "fp8_lora_backward", "fp8_lora_backward_workspace",
+                          "fp8_lora_backward", "fp8_lora_backward_workspace", "fp8_lora_backward_noalloc",
                           "fp8_nvfp4_quantize", "fp8_nvfp4_dequantize",
                           "fp8_status_string", "fp8_abi_version"}
     raw = ctypes.CDLL(fb.library_path)
@@ -47,8 +47,8 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.fp8_abi_version() == 5
-    for s in range(6):
+    assert lib.fp8_abi_version() == 6
+    for s in range(7):
         assert len(lib.fp8_status_string(s)) > 0
     assert lib.fp8_status_string(99) == b"unknown status"
 
@@ -205,6 +205,31 @@ def test_lora_backward_validation(lib):
     assert call(wsp=A16 + 128) == ALIGN                                 # workspace: 256 B
     assert call(db=A16 + 2, out=1) == ALIGN                             # fp32 gradients: 4 B
     assert call(db=A16 + 1) == ALIGN
+
+
+def test_lora_backward_noalloc_validation(lib):
+    """The no-allocation LoRA backward checks its arguments like
+    fp8_lora_backward and refuses problems whose workspace exceeds the fixed
+    scratch (before touching a device)."""
+    TOO_LARGE = 6
+    f = lib.fp8_lora_backward_noalloc
+
+    def call(m=64, n=128, k=256, r=16, dy=A16, x=A16, lb=A16, la=A16, db=A16, da=A16, out=0):
+        return f(dy, x, lb, la, m, n, k, r, db, da, out, None)
+
+    assert call(r=0) == INVALID and call(r=65) == INVALID
+    assert call(n=100) == SHAPE and call(m=-1) == SHAPE
+    assert call(out=2) == INVALID
+    assert call(n=0, k=0) == OK
+    assert call(dy=None) == INVALID and call(lb=None) == INVALID
+    assert call(dy=A16 + 8) == ALIGN and call(db=A16 + 2, out=1) == ALIGN
+    ws = ctypes.c_size_t(0)
+    m, n, k, r = 8192, 7168, 7168, 64
+    assert lib.fp8_lora_backward_workspace(m, n, k, r, ctypes.byref(ws)) == OK
+    assert ws.value <= fb.NOALLOC_SCRATCH_BYTES                # the documented fit
+    assert lib.fp8_lora_backward_workspace(4 * m, n, k, r, ctypes.byref(ws)) == OK
+    assert ws.value > fb.NOALLOC_SCRATCH_BYTES
+    assert call(m=4 * m, n=n, k=k, r=r) == TOO_LARGE
 
 
 def test_python_binding_rejects_host_tensors(lib):
