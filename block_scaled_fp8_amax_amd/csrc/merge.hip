@@ -138,22 +138,30 @@ __global__ __launch_bounds__(256) void merge_128_kernel(const uint16_t* __restri
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const uint32_t o = lofs + j * jstep;
-      uint32_t c[DW];
+      // the lane's codes in one dword: the first pair in the low half, the
+      // second (4 columns per lane) in the high half of the same register
+      uint32_t cw;
 #pragma unroll
       for (int d = 0; d < DW; ++d) {
         const float q0 = TINY ? f32_quot(bf_lo(wp[j * DW + d]), fb) : f32_quot_unit(bf_lo(wp[j * DW + d]), fb);
         const float q1 = TINY ? f32_quot(bf_hi(wp[j * DW + d]), fb) : f32_quot_unit(bf_hi(wp[j * DW + d]), fb);
-        c[d] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false) & 0xFFFFu;
+        // the low pair's conversion keeps the register's high half, which
+        // the second pair then overwrites: any prior content will do
+        if (d == 0)
+          cw = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, __float_as_int(q0), false);
+        else
+          cw = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, (int)cw, true);
       }
       if constexpr (DW == 2)
-        store_code<CACHED>(c[0] | (c[1] << 16), reinterpret_cast<uint32_t*>(qb + o));
+        store_code<CACHED>(cw, reinterpret_cast<uint32_t*>(qb + o));
       else
-        *reinterpret_cast<uint16_t*>(qb + o) = (uint16_t)c[0];
+        *reinterpret_cast<uint16_t*>(qb + o) = (uint16_t)cw;
       if constexpr (DQ) {
         uint32_t dv[DW];
 #pragma unroll
         for (int d = 0; d < DW; ++d) {
-          const v2f dq = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[d], false);
+          const v2f dq = d == 0 ? __builtin_amdgcn_cvt_pk_f32_fp8((int)cw, false)
+                                : __builtin_amdgcn_cvt_pk_f32_fp8((int)cw, true);
           dv[d] = pack_bf16x2(dq[0] * fb.s, dq[1] * fb.s);
         }
         if constexpr (DW == 2)
