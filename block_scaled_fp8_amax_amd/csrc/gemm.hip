@@ -514,7 +514,9 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmParams p) {
           if constexpr (MODE == kF32xMX)
             part[ni & 1][mi] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[mi], bfr[ni], zero, 0, 0, 0, 127,
                                                                                 0, xb[ni]);
-          else
+          else  // literal zero scale operands: the compiler emits the plain (unscaled)
+                // v_mfma_f32_16x16x128_f8f6f4; the neutral E8M0 scale 127 gives the scaled
+                // form with scale registers, measured 11% slower in this kernel (C2, C3)
             part[ni & 1][mi] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[mi], bfr[ni], zero, 0, 0, 0, 0, 0, 0);
           if (ni > 0) {
 #pragma unroll
