@@ -151,44 +151,46 @@ __device__ __forceinline__ void group_rows(const GemmParams& p, int g, int* lo, 
   *hi = clamp_int(p.offsets[g + 1], *lo, total);
 }
 
-// s_pref: LDS of groups + 1 ints; returns the tile count.
+// s_incl: LDS of `groups` ints, s_incl[g] = m-tiles of groups 0..g (the
+// m-tiles before group g are s_incl[g - 1], 0 for g = 0); returns the tile
+// count.
 template <int BM>
-__device__ __forceinline__ int grouped_prefix(const GemmParams& p, int* s_pref, int nthreads) {
+__device__ __forceinline__ int grouped_prefix(const GemmParams& p, int* s_incl, int nthreads) {
   const int groups = p.groups;
   const int t = threadIdx.x;
   for (int g = t; g < groups; g += nthreads) {
     int lo, hi;
     group_rows(p, g, &lo, &hi);
-    s_pref[g + 1] = (hi - lo + BM - 1) / BM;
+    s_incl[g] = (hi - lo + BM - 1) / BM;
   }
-  if (t == 0) s_pref[0] = 0;
   __syncthreads();
-  for (int d = 1; d < groups; d <<= 1) {  // inclusive scan of s_pref[1..groups]
+  for (int d = 1; d < groups; d <<= 1) {  // inclusive scan
     int v[4];
     int cnt = 0;
-    for (int g = t; g < groups; g += nthreads) v[cnt++] = (g >= d) ? s_pref[g + 1 - d] : 0;
+    for (int g = t; g < groups; g += nthreads) v[cnt++] = (g >= d) ? s_incl[g - d] : 0;
     __syncthreads();
     cnt = 0;
-    for (int g = t; g < groups; g += nthreads) s_pref[g + 1] += v[cnt++];
+    for (int g = t; g < groups; g += nthreads) s_incl[g] += v[cnt++];
     __syncthreads();
   }
-  return s_pref[groups] * p.tiles_n;
+  return s_incl[groups - 1] * p.tiles_n;
 }
 
 // Tile L (< the tile count) -> group, first row, rows, n-tile.
 template <int BM>
-__device__ __forceinline__ void grouped_locate(const GemmParams& p, const int* s_pref, int L,
+__device__ __forceinline__ void grouped_locate(const GemmParams& p, const int* s_incl, int L,
                                                int* g_out, int64_t* row0, int* rows, int* tn_out) {
   const int tiles_n = p.tiles_n;
   const int slot = L / tiles_n;
-  int lo = 0, hi = p.groups - 1;  // g with s_pref[g] <= slot < s_pref[g+1]
+  int lo = 0, hi = p.groups - 1;  // g with s_incl[g - 1] <= slot < s_incl[g]
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (s_pref[mid] <= slot) lo = mid; else hi = mid - 1;
+    if (s_incl[mid - 1] <= slot) lo = mid; else hi = mid - 1;
   }
   const int g = lo;
-  const int tmg = s_pref[g + 1] - s_pref[g];
-  const int r = L - s_pref[g] * tiles_n;
+  const int before = g > 0 ? s_incl[g - 1] : 0;
+  const int tmg = s_incl[g] - before;
+  const int r = L - before * tiles_n;
   const int band = p.band > 0 && p.band < tmg ? p.band : tmg;
   const int per_band = band * tiles_n;
   const int b = r / per_band, rr = r - b * per_band;
@@ -207,9 +209,17 @@ __device__ __forceinline__ void grouped_locate(const GemmParams& p, const int* s
 // chunks of several K steps, 4 bytes per row and step: one fp32 scale, or
 // the four E8M0 scales of the step's 1x32 blocks.  A chunk of SC steps is
 // laid out as [block of 64/SC rows][K step][64/SC rows] x 4 bytes, so that
-// one 64-lane load fills one block.
+// one 64-lane dword load fills one block.  E8M0 B scales whose 4-step
+// pieces are 16-byte aligned (K a multiple of 512, scale array 16-byte
+// aligned) are loaded instead 16 bytes per column and lane, a chunk laid
+// out as [column][K step] x 4 bytes: one load per 64 columns and 4 steps
+// in place of 4 dword loads that each touch 16 scale rows (on the grouped
+// MoE GEMM the dword loads cost 10% against no B-scale loads at all, the
+// 16-byte loads about 5%).
 constexpr int kLdsMax = 160 * 1024;
-constexpr int kGroupTable = 1025 * 4;           // grouped: m-tile prefix of up to 1024 groups
+constexpr int kGroupTable = 1024 * 4;           // grouped: m-tile prefix of up to 1024 groups
+// (1024 and not 1025 ints: with 3 stages, both 4-step scale rings and the
+// table, a 128x256 or 256x128 tile fills the 160 KiB of LDS exactly)
 
 // LDS bytes of a kernel with 3 stages and chunks of sa (A) and sb (B) steps
 constexpr int pp_lds_bytes(int bm, int bn, bool b_mx, bool grouped, int sa, int sb) {
@@ -260,7 +270,7 @@ struct Layout {
 // chunks (the chunk starting at step kb is issued with the loads of stage
 // kb), group 1 the B scales (E8M0 B in chunks too).  A stage is read at
 // half-steps 2kb and 2kb+1 and refilled from half-step 2kb+6 on (3 stages).
-template <int MODE, bool OUT_F32, bool GROUPED, int BM, int BN>
+template <int MODE, bool OUT_F32, bool GROUPED, int BM, int BN, bool BVEC>
 __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmParams p) {
   constexpr int STAGES = 3, NW = 8;
   constexpr int WMB = BM / 64;                 // 64-row blocks of the tile
@@ -276,6 +286,8 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmParams p) {
   constexpr int RPLA = 64 / SCA, RPLB = 64 / SCB;
   constexpr int LPWA = BM / RPLA / 4, LPWB = B_MX ? BN / RPLB / 4 : 1;
   using L = Layout<BM, BN, STAGES, B_MX, SCA, SCB>;
+  // BVEC: E8M0 B scales taken 16 bytes (4 K steps) per column and lane
+  static_assert(!BVEC || (B_MX && SCB == 4 && BN % 64 == 0), "vector B-scale chunks");
   __shared__ __attribute__((aligned(16))) uint8_t smem[L::kBytes];
   __shared__ int s_grp[GROUPED ? kGroupTable / 4 : 1];   // grouped: m-tile prefix
 
@@ -374,14 +386,24 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmParams p) {
     c_steps = SCA; c_rows = RPLA; c_loads = LPWA;
   } else {
     c_base = sb8 + n0 * (K / 32);
+    if constexpr (BVEC) {
+      c_off[0] = (uint32_t)((gw * 64 + lane) * (K / 32));
+      c_loads = gw < BN / 64 ? 1 : 0;
+    } else {
 #pragma unroll
-    for (int j = 0; j < LPW; ++j) c_off[j] = (uint32_t)(((j * 4 + gw) * RPLB + lane % RPLB) * (K / 32));
+      for (int j = 0; j < LPW; ++j) c_off[j] = (uint32_t)(((j * 4 + gw) * RPLB + lane % RPLB) * (K / 32));
+      c_loads = B_MX ? LPWB : 0;
+    }
     c_ring = L::kRingB;
-    c_steps = SCB; c_rows = RPLB; c_loads = B_MX ? LPWB : 0;
+    c_steps = SCB; c_rows = RPLB;
   }
   const uint32_t c_chunk = grp == 0 ? L::kChunkA : L::kChunkB;
   auto issue_chunk = [&](int c) {
     const uint32_t cbase = lds0 + c_ring + (c & 1) * c_chunk;
+    if (BVEC && grp == 1) {
+      if (c_loads) dma16(c_base, c_off[0] + (uint32_t)c * 16, cbase + gw * 1024);
+      return;
+    }
     int ks = c * c_steps + lane / c_rows;
     ks = ks < KB ? ks : KB - 1;
 #pragma unroll
@@ -450,6 +472,7 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmParams p) {
     // column c: sSCB[(c / RPLB) * 64 + c % RPLB]
     const uint32_t* sSCA = reinterpret_cast<const uint32_t*>(smem + L::kRingA + ((kb / SCA) & 1) * L::kChunkA) + (kb % SCA) * RPLA;
     const uint32_t* sSCB = reinterpret_cast<const uint32_t*>(smem + L::kRingB + ((kb / SCB) & 1) * L::kChunkB) + (kb % SCB) * RPLB;
+    const uint32_t* sSCBv = reinterpret_cast<const uint32_t*>(smem + L::kRingB + ((kb / SCB) & 1) * L::kChunkB) + (kb % SCB);
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
       const int ar = wm * 64 + mi * 16 + fr;
@@ -477,7 +500,8 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmParams p) {
       if constexpr (do_load) {
         if (4 + ni < PER) issue_one(kb + STAGES - 1, 4 + ni);
       }
-      if constexpr (B_MX) xb[ni] = (int)((sSCB[(bc / RPLB) * 64 + bc % RPLB] >> (8 * fg)) & 0xFFu);
+      if constexpr (BVEC) xb[ni] = (int)((sSCBv[bc * SCB] >> (8 * fg)) & 0xFFu);
+      else if constexpr (B_MX) xb[ni] = (int)((sSCB[(bc / RPLB) * 64 + bc % RPLB] >> (8 * fg)) & 0xFFu);
     }
     if constexpr (MODE == kF32xF32) sbk = __uint_as_float(sSB[(wn >> 1) * SLB]);
     if constexpr (do_load) {
@@ -553,9 +577,11 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmParams p) {
 
   // wait until this wave's share of stage kb has landed (the next stage may
   // stay in flight); then the barrier makes every share visible
+  // (BVEC: a B-scale chunk issued behind stage kb+1 may stay in flight too)
   auto wait_stage = [&](int kb) {
     if (kb + 1 >= KB) wait_vmcnt(0);
     else if (s_load) wait_vmcnt(PER);
+    else if (BVEC && grp == 1 && c_loads && (kb + 1) % SCB == 0) wait_vmcnt(PER);
     else wait_vmcnt(PER - 1);
   };
   auto half_barrier = [&]() {
@@ -643,13 +669,17 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmParams p) {
   }  // tile loop
 }
 
-template <int MODE, bool GROUPED, int BM, int BN>
+template <int MODE, bool GROUPED, int BM, int BN, bool BVEC = false>
 static void launch_pp(const GemmParams& p, dim3 grid, bool out_f32, hipStream_t stream) {
   if (out_f32)
-    hipLaunchKernelGGL((gemm_pp_kernel<MODE, true, GROUPED, BM, BN>), grid, dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((gemm_pp_kernel<MODE, true, GROUPED, BM, BN, BVEC>), grid, dim3(512), 0, stream, p);
   else
-    hipLaunchKernelGGL((gemm_pp_kernel<MODE, false, GROUPED, BM, BN>), grid, dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((gemm_pp_kernel<MODE, false, GROUPED, BM, BN, BVEC>), grid, dim3(512), 0, stream, p);
 }
+// E8M0 B scales in 16-byte pieces: every column's chunk of 4 K steps is
+// 16-byte aligned and inside its row when K is a multiple of 512 and the
+// scale array is 16-byte aligned
+static bool b_scales_vec(const void* sb, int64_t k) { return k % 512 == 0 && (uintptr_t)sb % 16 == 0; }
 
 // Dense: 128x256 tiles (256x128 when n is not a multiple of 256), 3 stages
 // (151 or 153.5 KiB of LDS with the A-scale ring, one workgroup per CU); a tile moves 48 KiB per K step
@@ -677,6 +707,9 @@ hipError_t launch_gemm(const uint8_t* a, const void* sa, int a_kind, const uint8
   if (a_kind == 1 && b_kind == 2) {
     if (wide) launch_pp<kF32xF32, false, 128, 256>(p, grid, out_f32, stream);
     else launch_pp<kF32xF32, false, 256, 128>(p, grid, out_f32, stream);
+  } else if (b_scales_vec(sb, k)) {
+    if (wide) launch_pp<kMXxMX, false, 128, 256, true>(p, grid, out_f32, stream);
+    else launch_pp<kMXxMX, false, 256, 128, true>(p, grid, out_f32, stream);
   } else {
     if (wide) launch_pp<kMXxMX, false, 128, 256>(p, grid, out_f32, stream);
     else launch_pp<kMXxMX, false, 256, 128>(p, grid, out_f32, stream);
@@ -705,7 +738,10 @@ hipError_t launch_grouped_gemm(const uint8_t* a, const void* sa, int a_kind, con
   // multiple of the 8 XCDs
   const int wgs = num_cu >= 8 ? num_cu / 8 * 8 : 8;
   dim3 grid((unsigned)wgs);
-  if (b_kind == 0) {
+  if (b_kind == 0 && b_scales_vec(sb, k)) {
+    if (wide) launch_pp<kF32xMX, true, 128, 256, true>(p, grid, out_f32, stream);
+    else launch_pp<kF32xMX, true, 256, 128, true>(p, grid, out_f32, stream);
+  } else if (b_kind == 0) {
     if (wide) launch_pp<kF32xMX, true, 128, 256>(p, grid, out_f32, stream);
     else launch_pp<kF32xMX, true, 256, 128>(p, grid, out_f32, stream);
   } else {

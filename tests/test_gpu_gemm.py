@@ -166,7 +166,8 @@ def test_grouped_edge_cases(bkind, n):
 @pytest.mark.parametrize("bkind", ["1x32", "128x128"])
 def test_grouped_scale_chunk_tails(bkind, n, k):
     """K steps (K / 128) that are not a multiple of the scale-chunk length
-    (4 steps, or 2 for 256x128 tiles with E8M0 B), with both tile shapes."""
+    (4 steps), with both tile shapes; K / 32 not a multiple of 16 (E8M0 B
+    scales in dword pieces)."""
     sizes = [130, 0, 257, 64]
     g = len(sizes)
     off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
@@ -209,6 +210,78 @@ def test_grouped_many_groups(bkind):
         lo, hi = off[e], off[e + 1]
         if hi > lo:
             assert gemm.normwise_rel_err(y32[lo:hi], ref[e]) <= TOL, e
+
+
+@pytest.mark.parametrize("k", [512, 384])
+def test_grouped_max_groups(k):
+    """The largest group count the library takes (1024; the kernel keeps one
+    m-tile prefix per group in LDS), E8M0 B with K a multiple of 512 (B scales
+    in 16-byte pieces) and not; every nonempty group is checked."""
+    rng = np.random.default_rng(33)
+    g, n = 1024, 256
+    sizes = rng.integers(0, 65, g)
+    sizes[rng.choice(g, g // 8, replace=False)] = 0
+    sizes[-1] = 3                                   # the last table entry holds rows
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    total = int(off[-1])
+    aq, sa = _q(_rand_bf16((total, k), 1.0, 60), "1x128")
+    bq, sb = _q(_rand_bf16((g * n, k), 0.02, 61), "1x32")
+    bq = bq.view(g, n, k)
+    sb = sb.view(g, n, k // 32)
+    offt = torch.from_numpy(off).cuda()
+    print(f"[grouped] {g} groups k={k} total rows {total}", flush=True)
+    y32 = _grouped(aq, sa, bq, sb, "1x32", offt).cpu().numpy()
+    ref = gemm.grouped_gemm_ref(aq.cpu().numpy(), sa.cpu().numpy(), "1x128", bq.cpu().numpy(),
+                                sb.cpu().numpy(), "1x32", off)
+    for e in range(g):
+        lo, hi = off[e], off[e + 1]
+        if hi > lo:
+            assert gemm.normwise_rel_err(y32[lo:hi], ref[e]) <= TOL, e
+
+
+def _offset_copy(t, byte_offset):
+    """A contiguous copy of t whose data starts byte_offset bytes past a
+    256-byte aligned allocation (4-byte aligned, not 16-byte aligned)."""
+    nbytes = t.numel() * t.element_size()
+    buf = torch.empty(nbytes + 256, dtype=torch.uint8, device=t.device)
+    view = buf[byte_offset:byte_offset + nbytes].view(t.dtype).view(t.shape)
+    view.copy_(t)
+    assert view.data_ptr() % 16 == byte_offset % 16
+    return view
+
+
+@pytest.mark.parametrize("n", [256, 384])
+def test_b_scale_load_paths_agree(n):
+    """E8M0 B scales 16-byte aligned (loaded 16 bytes per column) and only
+    4-byte aligned (loaded by dwords) give the same bytes, for the grouped
+    fp32 x MXFP8 GEMM and the dense MXFP8 x MXFP8 GEMM, both tile shapes."""
+    sizes = [200, 0, 129, 64]
+    g, k = len(sizes), 1024
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    total = int(off[-1])
+    aq, sa = _q(_rand_bf16((total, k), 1.0, 70), "1x128")
+    bq, sb = _q(_rand_bf16((g * n, k), 0.02, 71), "1x32")
+    bq = bq.view(g, n, k)
+    sb = sb.view(g, n, k // 32)
+    offt = torch.from_numpy(off).cuda()
+    print(f"[grouped] B-scale load paths n={n}", flush=True)
+    y_vec = _grouped(aq, sa, bq, sb, "1x32", offt)
+    y_dw = _grouped(aq, sa, bq, _offset_copy(sb, 4), "1x32", offt)
+    assert torch.equal(y_vec.view(torch.int32), y_dw.view(torch.int32))
+    ref = gemm.grouped_gemm_ref(aq.cpu().numpy(), sa.cpu().numpy(), "1x128", bq.cpu().numpy(),
+                                sb.cpu().numpy(), "1x32", off)
+    y = y_vec.cpu().numpy()
+    for e in range(g):
+        lo, hi = off[e], off[e + 1]
+        assert gemm.normwise_rel_err(y[lo:hi], ref[e]) <= TOL, e
+    ma, sma = _q(_rand_bf16((300, k), 1.0, 72), "1x32")
+    mb, smb = _q(_rand_bf16((n, k), 1.0, 73), "1x32")
+    print(f"[gemm] MX x MX B-scale load paths n={n}", flush=True)
+    d_vec = _gemm(ma, sma, "1x32", mb, smb, "1x32")
+    d_dw = _gemm(ma, sma, "1x32", mb, _offset_copy(smb, 4), "1x32")
+    assert torch.equal(d_vec.view(torch.int32), d_dw.view(torch.int32))
+    ref = gemm.gemm_ref32(ma.cpu().numpy(), sma.cpu().numpy(), "1x32", mb.cpu().numpy(), smb.cpu().numpy(), "1x32")
+    assert gemm.normwise_rel_err(d_vec.cpu().numpy(), ref) <= TOL
 
 
 def test_grouped_moe_full():
