@@ -15,13 +15,20 @@
 // Layout: one 256-thread workgroup per 128x128 block; wave w owns rows
 // 32w .. 32w+31.  A lane owns CPL consecutive columns (4 for ranks up to
 // 16, 2 above), so LPR = 128/CPL lanes cover a block row and a wave-wide
-// load covers 64/LPR rows.  All of the wave's W loads are issued first
-// (the 128x128 bf16 block is held in registers, 32 dwords per lane).  B's
-// block rows go to LDS as fp32 (read back as 16-byte broadcasts) and the
-// lane's A columns to registers; ranks from r up to the template's RMAX
-// are zero, which leaves the sequential sum unchanged bit for bit
-// (acc + 0 * 0 = acc), so the rank loop has no branches.  The update costs
-// RMAX fused multiply-adds per element on the vector ALU.
+// load covers 64/LPR rows.  Every load of the workgroup's block is issued
+// up front, in the order B block, A columns, W rows (the 128x128 bf16 block
+// is held in registers, 32 dwords per lane), so that B's LDS stores wait
+// only for B and the merge of each W row only for that row; the barrier
+// after the LDS stores waits on LDS alone.  B's block rows go to LDS as
+// fp32 (read back as 16-byte broadcasts) and the lane's A columns to
+// registers; ranks from r up to the template's RMAX are zero, which leaves
+// the sequential sum unchanged bit for bit (acc + 0 * 0 = acc), so the rank
+// loop has no branches.  The loads of B and A are issued for every rank at
+// a rank clamped below r and zeroed afterwards: a load under a branch
+// waited for everything in flight, which serialized the 8 B loads of a
+// thread behind the W block (rank 16: 60.0 to 54.0 us, rank 64: 324 to
+// 202 us at 7168x7168).  The update costs RMAX fused multiply-adds per
+// element on the vector ALU.
 #include <type_traits>
 
 #include "device.h"
@@ -55,7 +62,29 @@ __global__ __launch_bounds__(256) void merge_128_kernel(const uint16_t* __restri
   const uint32_t jstep = (uint32_t)(RPI * k);
   const uint8_t* wb = reinterpret_cast<const uint8_t*>(w + blk);   // byte offsets 2 * o
 
-  // 1. the wave's 32 rows of W, all loads in flight
+  // Loads in the order B block, A columns, W rows, with compiler barriers
+  // between the groups: B's LDS stores then wait only for B, and the merge
+  // waits for each W row as it arrives.
+  constexpr int BPT = 128 * RMAX / 256;   // B elements per thread
+  uint32_t braw[BPT];
+  // (every load is issued, at a clamped rank below r, so that none waits
+  // behind a branch; ranks >= r are then zeroed)
+#pragma unroll
+  for (int n = 0; n < BPT; ++n) {
+    const int i = t + 256 * n;
+    const int rr = i / RMAX, cc = i % RMAX;
+    braw[n] = (uint32_t)lb[(row0 + rr) * r + (cc < r ? cc : r - 1)];
+  }
+  asm volatile("" ::: "memory");
+  uint32_t araw[RMAX][DW];
+#pragma unroll
+  for (int i = 0; i < RMAX; ++i) {
+    const int ic = i < r ? i : r - 1;
+    // dword loads: lora_a is only required to be 4-byte aligned
+#pragma unroll
+    for (int d = 0; d < DW; ++d) araw[i][d] = *reinterpret_cast<const uint32_t*>(la + (int64_t)ic * k + col + 2 * d);
+  }
+  asm volatile("" ::: "memory");
   uint32_t wp[32];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
@@ -68,30 +97,25 @@ __global__ __launch_bounds__(256) void merge_128_kernel(const uint16_t* __restri
       wp[j] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(wb + 2 * o));
     }
   }
-  // 2. B block [128 x r] -> LDS as fp32, ranks >= r zero
-  for (int i = t; i < 128 * RMAX; i += 256) {
-    const int rr = i / RMAX, cc = i % RMAX;
-    sB[i] = cc < r ? __uint_as_float((uint32_t)lb[(row0 + rr) * r + cc] << 16) : 0.f;
+  asm volatile("" ::: "memory");
+#pragma unroll
+  for (int n = 0; n < BPT; ++n) {
+    const int cc = (t + 256 * n) % RMAX;
+    sB[t + 256 * n] = cc < r ? __uint_as_float(braw[n] << 16) : 0.f;
   }
-  // 3. this lane's columns of A -> registers, ranks >= r zero
   float a[RMAX][CPL];
 #pragma unroll
-  for (int i = 0; i < RMAX; ++i) {
-    uint32_t v[DW];
-#pragma unroll
-    for (int d = 0; d < DW; ++d) v[d] = 0;
-    if (i < r) {
-      // dword loads: lora_a is only required to be 4-byte aligned
-#pragma unroll
-      for (int d = 0; d < DW; ++d) v[d] = *reinterpret_cast<const uint32_t*>(la + (int64_t)i * k + col + 2 * d);
-    }
+  for (int i = 0; i < RMAX; ++i)
 #pragma unroll
     for (int d = 0; d < DW; ++d) {
-      a[i][2 * d] = bf_lo(v[d]);
-      a[i][2 * d + 1] = bf_hi(v[d]);
+      a[i][2 * d] = i < r ? bf_lo(araw[i][d]) : 0.f;
+      a[i][2 * d + 1] = i < r ? bf_hi(araw[i][d]) : 0.f;
     }
-  }
-  __syncthreads();
+  // B's LDS stores land before the barrier; the W loads may stay in flight
+  // (__syncthreads would wait for them as well)
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 
   // 4. merge in place: W' = RN_bf16(W + RN_bf16(sum_r B[n,r] A[r,k]))
   uint32_t m = 0;
