@@ -28,33 +28,38 @@ __global__ __launch_bounds__(kDqThreads) void dequant_kernel(const u32x2* __rest
                                                              uint32_t cpr, int64_t cols, const void* __restrict__ scale,
                                                              u32x4* __restrict__ x) {
   const uint32_t first = blockIdx.x * (uint32_t)(kDqThreads * kDqU) + threadIdx.x;
+  // codes and scales of every chunk loaded before any is used (indices past
+  // the end read the last chunk and are not stored), so that no load waits
+  // behind another
   u32x2 c[kDqU];
+  float s[kDqU];
 #pragma unroll
   for (int u = 0; u < kDqU; ++u) {
-    const uint32_t idx = first + u * kDqThreads;
-    c[u] = idx < nchunks ? __builtin_nontemporal_load(q + idx) : (u32x2){0u, 0u};
+    const uint32_t i0 = first + u * kDqThreads;
+    const uint32_t idx = i0 < nchunks ? i0 : nchunks - 1;
+    c[u] = __builtin_nontemporal_load(q + idx);
+    if constexpr (KIND == 0) {
+      // row blocks never straddle rows, so the scales are in chunk order:
+      // 4 chunks per 1x32 block
+      s[u] = e8m0_val(reinterpret_cast<const uint8_t*>(scale)[idx >> 2]);
+    } else if constexpr (KIND == 1) {
+      s[u] = reinterpret_cast<const float*>(scale)[idx >> 4];   // 16 chunks per 1x128 tile
+    } else {
+      const uint32_t row = idx / cpr;                   // cpr = cols / 8 chunks per row
+      const int64_t col = (int64_t)(idx - row * cpr) * 8;
+      s[u] = reinterpret_cast<const float*>(scale)[(int64_t)(row / 128) * (cols / 128) + col / 128];
+    }
   }
 #pragma unroll
   for (int u = 0; u < kDqU; ++u) {
     const uint32_t idx = first + u * kDqThreads;
     if (idx >= nchunks) continue;
-    float s;
-    if constexpr (KIND == 0) {
-      // row blocks never straddle rows, so the scales are in chunk order:
-      // 4 chunks per 1x32 block
-      s = e8m0_val(reinterpret_cast<const uint8_t*>(scale)[idx >> 2]);
-    } else if constexpr (KIND == 1) {
-      s = reinterpret_cast<const float*>(scale)[idx >> 4];   // 16 chunks per 1x128 tile
-    } else {
-      const uint32_t row = idx / cpr;                   // cpr = cols / 8 chunks per row
-      const int64_t col = (int64_t)(idx - row * cpr) * 8;
-      s = reinterpret_cast<const float*>(scale)[(int64_t)(row / 128) * (cols / 128) + col / 128];
-    }
     float d[8];
     decode4_e4m3(c[u].x, d);
     decode4_e4m3(c[u].y, d + 4);
-    const u32x4 o = {pack_bf16x2(d[0] * s, d[1] * s), pack_bf16x2(d[2] * s, d[3] * s),
-                     pack_bf16x2(d[4] * s, d[5] * s), pack_bf16x2(d[6] * s, d[7] * s)};
+    const float su = s[u];
+    const u32x4 o = {pack_bf16x2(d[0] * su, d[1] * su), pack_bf16x2(d[2] * su, d[3] * su),
+                     pack_bf16x2(d[4] * su, d[5] * su), pack_bf16x2(d[6] * su, d[7] * su)};
     __builtin_nontemporal_store(o, x + idx);
   }
 }

