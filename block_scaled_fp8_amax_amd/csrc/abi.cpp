@@ -320,7 +320,8 @@ int fp8_nvfp4_dequantize(const uint8_t* q, const uint8_t* block_scale, const flo
   if (int s = nvfp4_shape(rows, cols, rows_per_tensor)) return s;
   if (rows == 0 || cols == 0) return FP8_OK;
   if (!q || !block_scale || !global_scale || !x) return FP8_ERR_INVALID_ARG;
-  // codes are read 8 bytes (one 1x16 block) per lane
+  // codes are read a dword (half a 1x16 block) at a time; q keeps the 8-byte
+  // alignment of fp8_nvfp4_quantize's code buffer
   if (!aligned(q, 8) || !aligned(global_scale, 4) || !aligned(x, 16)) return FP8_ERR_ALIGN;
   DeviceInfo* dev = nullptr;
   if (int s = current_device(&dev)) return s;

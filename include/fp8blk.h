@@ -367,7 +367,7 @@ int fp8_nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ro
  *   x = RN_bf16(RN32(e2m1(code) * RN32(e4m3(S) * g))), the value
  * fp8_nvfp4_quantize writes to xdq.  Defined by: [prequant] "Formats"
  * (serving loads the packed weights); arguments and shape as there (q
- * 8-byte aligned: one 1x16 block of codes is read as 8 bytes).
+ * 8-byte aligned, as fp8_nvfp4_quantize requires of its code buffer).
  */
 int fp8_nvfp4_dequantize(const uint8_t* q, const uint8_t* block_scale, const float* global_scale,
                          int64_t rows, int64_t cols, int64_t rows_per_tensor, uint16_t* x, void* stream);
