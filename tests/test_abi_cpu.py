@@ -392,4 +392,4 @@ def test_nvfp4_validation(lib):
     assert d(None, None, None, 0, 32, 1, None, None) == OK
     assert d(A16, None, A16, 4, 32, 4, A16, None) == INVALID
     assert d(A16, A16, A16, 4, 32, 4, A16 + 8, None) == ALIGN
-    assert d(A16 + 4, A16, A16, 4, 32, 4, A16, None) == ALIGN      # codes: 8 B (one 1x16 block per lane)
+    assert d(A16 + 4, A16, A16, 4, 32, 4, A16, None) == ALIGN      # codes: 8-byte aligned, as the quantize requires
