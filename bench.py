@@ -18,7 +18,11 @@ the stream the kernel runs on, around a back-to-back loop of it run right
 after the timed region (its time between per-launch events inside whole
 steps, from the untimed pass below, is reported beside it).  ``components`` gives every kernel's own time, GB/s and
 roofline fraction from a separate, untimed pass with events around each
-launch.
+launch.  ``device_copy`` is the runtime's plain 512 MiB device-to-device
+copy timed the same way after everything else, and each bandwidth-bound
+component also gives its fraction of that copy's rate (``copy_frac``): a
+second reference beside the 8 TB/s peak (the runtime's copy itself streams
+well below the quantize kernels, so the fraction can exceed 1).
 
 Other workloads (``--config``) print the same kind of line for their own
 path: dense (the DeepSeek-V3-shaped dense projection: W 2048x7168 quantized
@@ -736,6 +740,25 @@ def _spin_ms(ms):
     torch.cuda._sleep(int(min(ms, 2000.0) * _SPIN_PER_MS))
 
 
+def device_copy_gbs(nbytes=1 << 29, reps=5):
+    """Read + write bytes per second of a plain device-to-device copy of
+    nbytes (twice the Infinity Cache, so it streams from HBM), on the
+    current stream between one event pair."""
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    return 2.0 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+
+
 def run(args):
     fb = _lib()
     dev = "cuda"
@@ -805,6 +828,10 @@ def run(args):
             c["TFLOP/s"] = wl.kflops[name] / (ms * 1e-3) / 1e12
             c["mfma_frac"] = c["TFLOP/s"] / FP8_PEAK_TFLOPS
         components[name] = c
+    copy_gbs = device_copy_gbs()
+    for name, c in components.items():
+        if "GB/s" in c and name not in wl.kflops:
+            c["copy_frac"] = c["GB/s"] / copy_gbs
 
     if wl.bound == "mfma":
         achieved = wl.kflops[wl.dominant] / (dom_ms * 1e-3) / 1e12
@@ -837,6 +864,7 @@ def run(args):
         "config": wl.cfg,
         "components": components,
         "roofline": roof,
+        "device_copy": {"GB/s": copy_gbs, "bytes_per_copy": 2 * (1 << 29)},
     }
     if not args.no_cpu_baseline:
         with _one_thread():
