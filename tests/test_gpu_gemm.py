@@ -313,6 +313,7 @@ def test_grouped_moe_full():
     groups = sorted(set([int(order[0]), int(order[-1]), int(order[len(order) // 2])] +
                         list(np.random.default_rng(5).choice(256, 5, replace=False))))
     _check_sampled_groups(y, y32, aq, sa, bq, sb, offn, groups, np.random.default_rng(6), "gate||up")
+    _check_group_boundaries(y, y32, aq, sa, bq, sb, offn, np.random.default_rng(9), "gate||up")
 
 
 def _check_sampled_groups(y, y32, aq, sa, bq, sb, offn, groups, rng, label, per_group=64):
@@ -336,6 +337,36 @@ def _check_sampled_groups(y, y32, aq, sa, bq, sb, offn, groups, rng, label, per_
         assert err <= TOL
         assert err64 <= TOL
         assert np.array_equal(bf16_bits(y[rows]), codec.f32_to_bf16(got))
+
+
+def _check_group_boundaries(y, y32, aq, sa, bq, sb, offn, rng, label, ncols=256):
+    """Every group's first and last row (the rows next to the group
+    boundaries, which start and end its m-tiles) on a sample of output
+    columns, against the fp64 product of the same sampled operands (the
+    kernel meets the 2e-3 bound against it as against the k-ordered fp32
+    reference, which the sampled-group check above evaluates; the fp64
+    product is a library matmul, so every group fits in the test's time);
+    bf16 output equal to RN_bf16 of the fp32 output."""
+    n = y32.shape[1]
+    cols = np.sort(rng.choice(n, ncols, replace=False))
+    colt = torch.from_numpy(cols).cuda()
+    worst = 0.0
+    for g in range(len(offn) - 1):
+        lo, hi = int(offn[g]), int(offn[g + 1])
+        if hi == lo:
+            continue
+        rows = sorted({lo, hi - 1})
+        an, san = aq[rows].cpu().numpy(), sa[rows].cpu().numpy()
+        bn = bq[g].index_select(0, colt).cpu().numpy()
+        sbn = sb[g].index_select(0, colt).cpu().numpy()
+        ref = gemm.gemm_ref64(an, san, "1x128", bn, sbn, "1x32")
+        got = y32[rows].index_select(1, colt).cpu().numpy()
+        err = gemm.normwise_rel_err(got, ref)
+        worst = max(worst, err)
+        assert err <= TOL, f"{label} group {g}: err {err:.3e}"
+        assert np.array_equal(bf16_bits(y[rows].index_select(1, colt)), codec.f32_to_bf16(got))
+    print(f"[grouped] {label}: first and last row of all {len(offn) - 1} groups on {ncols} columns, worst normwise "
+          f"rel err {worst:.3e}", flush=True)
 
 
 def test_grouped_moe_down_full():
@@ -366,6 +397,7 @@ def test_grouped_moe_down_full():
     groups = sorted(set([int(order[0]), int(order[-1]), int(order[len(order) // 2])] +
                         list(np.random.default_rng(7).choice(256, 5, replace=False))))
     _check_sampled_groups(y, y32, hq, hs, bq, sb, offn, groups, np.random.default_rng(8), "down")
+    _check_group_boundaries(y, y32, hq, hs, bq, sb, offn, np.random.default_rng(10), "down")
 
 
 # ------------------------------------------------------------ gathered rows
