@@ -105,7 +105,8 @@ def test_dense_projection_full():
     d = dense_projection("cuda")
     aq, sa = _q(d["x"], "1x128")
     bq, sb = _q(d["w"], "128x128")
-    rows = np.sort(np.random.default_rng(3).choice(4096, 256, replace=False))
+    # random rows plus the first row of every 128-row tile (full rows: every n-tile)
+    rows = np.union1d(np.random.default_rng(3).choice(4096, 256, replace=False), np.arange(0, 4096, 128))
     _check_gemm(aq, sa, "1x128", bq, sb, "128x128", rows=rows, label="dense projection 4096x2048x7168")
 
 
@@ -113,7 +114,8 @@ def test_qat_gemm_full_sampled():
     d = qat_forward("cuda")
     aq, sa = _q(d["x"], "1x128")
     wq, ws = fb.fake_quant_merge(d["w"], d["lora_b"], d["lora_a"])
-    rows = np.sort(np.random.default_rng(4).choice(8192, 96, replace=False))
+    # random rows plus the last row of every 128-row tile (full rows: every n-tile)
+    rows = np.union1d(np.random.default_rng(4).choice(8192, 96, replace=False), np.arange(127, 8192, 128))
     _check_gemm(aq, sa, "1x128", wq.view(torch.uint8), ws, "128x128", rows=rows,
                 label="QAT 8192x7168x7168")
 
