@@ -154,7 +154,7 @@ def test_roundtrip_equals_fake_quant():
 
 def test_full_size_expert_pair():
     """gate and up (2048x7168 each) stacked: two tensors, their own scales;
-    sampled rows byte-exact, global scales and amax exact."""
+    every code and block scale byte-exact, global scales and amax exact."""
     fac = expert_factors()
     gate, up, _ = expert_weights(5, "cuda", fac)
     w = torch.cat([gate, up], 0)
@@ -164,12 +164,9 @@ def test_full_size_expert_pair():
     oA = nvfp4.tensor_amax(wb, 2048)
     assert_bytes_equal(A.cpu().numpy(), oA, "tensor amax")
     assert_bytes_equal(gs.cpu().numpy(), nvfp4.global_scale(oA), "global scales")
-    rows = np.sort(np.random.default_rng(64).choice(4096, 48, replace=False))
-    for r in rows:
-        t = r // 2048
-        oq, ob, _, _, _ = nvfp4.quantize(wb[r:r + 1], 1, amax=oA[t:t + 1])
-        assert_bytes_equal(q[r:r + 1].cpu().numpy(), oq, f"row {r} codes")
-        assert_bytes_equal(bs[r:r + 1].view(torch.uint8).cpu().numpy(), ob, f"row {r} scales")
+    oq, ob, _, _, _ = nvfp4.quantize(wb, 2048, amax=oA)
+    assert_bytes_equal(q.cpu().numpy(), oq, "codes")
+    assert_bytes_equal(bs.view(torch.uint8).cpu().numpy(), ob, "block scales")
 
 
 def test_quantize_state_dict_nvfp4():
