@@ -101,6 +101,19 @@ def test_scale_placement_probe():
     _check_gemm(aq, sa, "1x128", bq, sb, "128x128", label="scale placement")
 
 
+def _check_whole_output64(aq, sa, ka, bq, sb, kb, label):
+    """Every output element: normwise error against the fp64 product within
+    the bound, and the bf16 output equal to RN_bf16 of the fp32 output."""
+    y32 = _gemm(aq, sa, ka, bq, sb, kb, torch.float32)
+    y16 = _gemm(aq, sa, ka, bq, sb, kb, torch.bfloat16)
+    ref64 = gemm.gemm_ref64(aq.cpu().numpy(), sa.cpu().numpy(), ka, bq.cpu().numpy(), sb.cpu().numpy(), kb)
+    y32n = y32.cpu().numpy()
+    err64 = gemm.normwise_rel_err(y32n, ref64)
+    print(f"[gemm] {label} whole output: normwise rel err vs fp64 {err64:.3e}", flush=True)
+    assert err64 <= TOL
+    assert np.array_equal(bf16_bits(y16), codec.f32_to_bf16(y32n))
+
+
 def test_dense_projection_full():
     d = dense_projection("cuda")
     aq, sa = _q(d["x"], "1x128")
@@ -108,6 +121,7 @@ def test_dense_projection_full():
     # random rows plus the first row of every 128-row tile (full rows: every n-tile)
     rows = np.union1d(np.random.default_rng(3).choice(4096, 256, replace=False), np.arange(0, 4096, 128))
     _check_gemm(aq, sa, "1x128", bq, sb, "128x128", rows=rows, label="dense projection 4096x2048x7168")
+    _check_whole_output64(aq, sa, "1x128", bq, sb, "128x128", "dense projection 4096x2048x7168")
 
 
 def test_qat_gemm_full_sampled():
@@ -118,6 +132,7 @@ def test_qat_gemm_full_sampled():
     rows = np.union1d(np.random.default_rng(4).choice(8192, 96, replace=False), np.arange(127, 8192, 128))
     _check_gemm(aq, sa, "1x128", wq.view(torch.uint8), ws, "128x128", rows=rows,
                 label="QAT 8192x7168x7168")
+    _check_whole_output64(aq, sa, "1x128", wq.view(torch.uint8), ws, "128x128", "QAT 8192x7168x7168")
 
 
 def test_determinism():
