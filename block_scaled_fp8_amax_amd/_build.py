@@ -9,6 +9,7 @@ import os
 import shutil
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -39,18 +40,25 @@ def build(verbose=False, save_temps=False):
     hipcc = _hipcc()
     bdir = os.path.join(ROOT, "_build")
     os.makedirs(bdir, exist_ok=True)
-    objs = []
-    for src in SOURCES:
+    def compile_one(src):
         obj = os.path.join(bdir, src.replace(".", "_") + ".o")
         cmd = [hipcc, *DEVICE_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
         if save_temps:
             cmd.insert(1, "--save-temps")
-        if verbose:
-            print(" ".join(cmd), flush=True)
         res = subprocess.run(cmd, cwd=bdir, capture_output=True, text=True)
         errs = "\n".join(ln for ln in (res.stdout + res.stderr).splitlines()
                          if "is not a recognized feature for this target" not in ln)
-        if res.returncode != 0:
+        return src, obj, cmd, res.returncode, errs
+
+    # the sources compile independently, so they go to hipcc side by side
+    workers = max(1, min(len(SOURCES), os.cpu_count() or 1, 8))
+    with ThreadPoolExecutor(max_workers=workers) as pool:
+        results = list(pool.map(compile_one, SOURCES))
+    objs = []
+    for src, obj, cmd, rc, errs in results:
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        if rc != 0:
             raise RuntimeError(f"hipcc failed on {src}:\n{errs}")
         if verbose and errs.strip():
             print(errs)
