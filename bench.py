@@ -152,16 +152,19 @@ def mx_workload(fb, dev):
     xs = torch.empty((64, 16), dtype=torch.uint8, device=dev)
     y = torch.empty((64, 256), dtype=torch.bfloat16, device=dev)
 
+    # W and X are quantized in one batched launch (the same bytes as two
+    # separate calls), then the MX x MX GEMM
     def launches(i):
-        return [("quantize_w_1x32", lambda: fb.fp8_block_quantize(w, "1x32", "ceil", wq, ws)),
-                ("quantize_x_1x32", lambda: fb.fp8_block_quantize(x, "1x32", "ceil", xq, xs)),
+        return [("quantize_w_x_1x32", lambda: fb.fp8_block_quantize_batch([(w, "1x32", "ceil", wq, ws),
+                                                                           (x, "1x32", "ceil", xq, xs)])),
                 ("gemm_mx", lambda: fb.fp8_block_scaled_gemm(xq, xs, "1x32", wq, ws, "1x32", y))]
 
     flops = 2.0 * 64 * 256 * 512
-    kbytes = {"quantize_w_1x32": 256 * 512 * 3 + 256 * 16, "quantize_x_1x32": 64 * 512 * 3 + 64 * 16,
+    kbytes = {"quantize_w_x_1x32": (256 + 64) * 512 * 3 + (256 + 64) * 16,
               "gemm_mx": 64 * 512 + 256 * 512 + 64 * 16 + 256 * 16 + 64 * 256 * 2}
-    cfg = {"workload": "MXFP8 small case: quantize W 256x512 and X 64x512 (1x32, E8M0), GEMM 64x256x512, "
-                       "bf16 out (launch-latency bound, not roofline-meaningful)", "m": 64, "n": 256, "k": 512}
+    cfg = {"workload": "MXFP8 small case: quantize W 256x512 and X 64x512 (1x32, E8M0) in one batched launch, "
+                       "GEMM 64x256x512, bf16 out (launch-latency bound, not roofline-meaningful)",
+           "m": 64, "n": 256, "k": 512}
     return Workload(launches, "gemm_mx", "mfma", flops, sum(kbytes.values()), kbytes, {"gemm_mx": flops}, cfg,
                     "TFLOP/s")
 
