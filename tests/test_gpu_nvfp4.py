@@ -154,7 +154,9 @@ def test_roundtrip_equals_fake_quant():
 
 def test_full_size_expert_pair():
     """gate and up (2048x7168 each) stacked: two tensors, their own scales;
-    every code and block scale byte-exact, global scales and amax exact."""
+    every code and block scale byte-exact, global scales and amax exact; the
+    dequantize of those codes equals the oracle's fake-quant values on every
+    element."""
     fac = expert_factors()
     gate, up, _ = expert_weights(5, "cuda", fac)
     w = torch.cat([gate, up], 0)
@@ -164,9 +166,12 @@ def test_full_size_expert_pair():
     oA = nvfp4.tensor_amax(wb, 2048)
     assert_bytes_equal(A.cpu().numpy(), oA, "tensor amax")
     assert_bytes_equal(gs.cpu().numpy(), nvfp4.global_scale(oA), "global scales")
-    oq, ob, _, _, _ = nvfp4.quantize(wb, 2048, amax=oA)
+    oq, ob, _, _, oxdq = nvfp4.quantize(wb, 2048, amax=oA)
     assert_bytes_equal(q.cpu().numpy(), oq, "codes")
     assert_bytes_equal(bs.view(torch.uint8).cpu().numpy(), ob, "block scales")
+    x = fb.nvfp4_dequantize(q, bs, gs, rows_per_tensor=2048)
+    torch.cuda.synchronize()
+    assert_bytes_equal(bf16_bits(x), oxdq, "dequantized pair")
 
 
 def test_quantize_state_dict_nvfp4():
