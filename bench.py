@@ -16,9 +16,13 @@ Prints one JSON line.  ``value`` is the step's throughput in GEMM TFLOP/s
 describes the dominant kernel (the GEMM): its average duration comes from HIP events on
 the stream the kernel runs on, around a back-to-back loop of it run right
 after the timed region (its time between per-launch events inside whole
-steps, from the untimed pass below, is reported beside it).  ``components`` gives every kernel's own time, GB/s and
-roofline fraction from a separate, untimed pass with events around each
-launch.  ``device_copy`` is the runtime's plain 512 MiB device-to-device
+steps, from the untimed pass below, is reported beside it).  ``components``
+gives, for every kernel of the step, its time alone (``us``: the kernel run
+back to back on the rotating inputs between one event pair, like the
+dominant call) with the GB/s and roofline fraction that follow from it, and
+its time inside whole steps (``us_in_step``: an untimed pass with an event
+pair around each launch; such markers read several microseconds high for a
+short kernel).  ``device_copy`` is the runtime's plain 512 MiB device-to-device
 copy timed the same way after everything else, and each bandwidth-bound
 component also gives its fraction of that copy's rate (``copy_frac``): a
 second reference beside the 8 TB/s peak (the runtime's copy itself streams
@@ -821,9 +825,32 @@ def run(args):
         for name, fn in wl.launches(i):
             comp.around(name, fn)
     torch.cuda.synchronize()
+    in_step = comp.mean_ms()
+
+    # every other kernel alone as well, back to back on the step's rotating
+    # inputs between one event pair, as the dominant call above: a marker
+    # pair around a single short launch reads several microseconds high
+    alone = {wl.dominant: dom_ms}
+    base = args.warmup + args.steps + nd
+    for name in in_step:
+        if name in alone:
+            continue
+        fns = [fn for i in range(nd) for n2, fn in wl.launches(base + i) if n2 == name]
+        a0 = torch.cuda.Event(enable_timing=True)
+        a1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        _spin_ms(1.5 * host_ms * nd + 2.0)
+        a0.record()
+        for fn in fns:
+            fn()
+        a1.record()
+        torch.cuda.synchronize()
+        alone[name] = a0.elapsed_time(a1) / len(fns)
+
     components = {}
-    for name, ms in comp.mean_ms().items():
-        c = {"us": ms * 1e3}
+    for name, ms_step in in_step.items():
+        ms = alone[name]
+        c = {"us": ms * 1e3, "us_in_step": ms_step * 1e3}
         if name in wl.kbytes:
             c["GB/s"] = wl.kbytes[name] / (ms * 1e-3) / 1e9
             c["hbm_frac"] = c["GB/s"] / HBM_PEAK_GBS
@@ -847,7 +874,7 @@ def run(args):
     roof["traffic"] = recorded_traffic(args.config)
     roof["kernel"] = wl.dominant
     roof["kernel_us"] = dom_ms * 1e3
-    roof["kernel_us_in_step"] = components[wl.dominant]["us"]
+    roof["kernel_us_in_step"] = components[wl.dominant]["us_in_step"]
     roof["host_enqueue_us_per_step"] = host_ms * 1e3
 
     if wl.unit == "TFLOP/s":
