@@ -176,8 +176,8 @@ def mx_workload(fb, dev):
 def qat_workload(fb, dev):
     import workloads
     M, N, K, R = 8192, 7168, 7168, 16
-    d = workloads.qat_forward(dev)
-    w, la, lb, x = d["w"], d["lora_a"], d["lora_b"], d["x"]
+    # two input sets (2 x 220 MB of W and X, more than the Infinity Cache)
+    sets = [workloads.qat_forward(dev), workloads.qat_forward(dev, seed=350)]
     wq = torch.empty((N, K), dtype=torch.uint8, device=dev)
     ws = torch.empty((N // 128, K // 128), dtype=torch.float32, device=dev)
     wdq = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
@@ -187,6 +187,8 @@ def qat_workload(fb, dev):
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
 
     def launches(i):
+        d = sets[i % 2]
+        w, la, lb, x = d["w"], d["lora_a"], d["lora_b"], d["x"]
         return [("merge_fake_quant_w", lambda: fb.fp8_fake_quant_merge(w, lb, la, wq, ws, wdq)),
                 ("fake_quant_x_1x128", lambda: fb.fp8_block_quantize(x, "1x128", "ceil", xq, xs, xdq)),
                 ("gemm", lambda: fb.fp8_block_scaled_gemm(xq, xs, "1x128", wq, ws, "128x128", y))]
@@ -268,10 +270,12 @@ def moe_workload(fb, dev):
     import workloads
     T, E, N, K = 16384, 256, 4096, 7168
     tok, off = workloads.zipf_routing()
-    x = workloads.moe_tokens(dev)
+    # two activation sets (2 x 235 MB, more than the 256 MB Infinity Cache)
+    # rotate through the per-token quantize
+    xsets = [workloads.moe_tokens(dev), workloads.moe_tokens(dev, seed=502)]
     xq = torch.empty((T, K), dtype=torch.uint8, device=dev)
     xs = torch.empty((T, K // 128), dtype=torch.float32, device=dev)
-    fb.fp8_block_quantize(x, "1x128", "ceil", xq, xs)
+    fb.fp8_block_quantize(xsets[0], "1x128", "ceil", xq, xs)
     idx = tok.to(dev)
     aq = xq.index_select(0, idx).contiguous()     # rows grouped by expert (gathered outside the timed region)
     sa = xs.index_select(0, idx).contiguous()
@@ -286,6 +290,7 @@ def moe_workload(fb, dev):
     y = torch.empty((total_m, N), dtype=torch.bfloat16, device=dev)
 
     def launches(i):
+        x = xsets[i % 2]
         return [("quantize_x_1x128", lambda: fb.fp8_block_quantize(x, "1x128", "ceil", xq, xs)),
                 ("grouped_gemm", lambda: fb.fp8_grouped_gemm(aq, sa, "1x128", bq, sb, "1x32", offt, y))]
 
@@ -308,7 +313,7 @@ def moe_gather_workload(fb, dev):
     import workloads
     T, E, N, K = 16384, 256, 4096, 7168
     tok, off = workloads.zipf_routing()
-    x = workloads.moe_tokens(dev)
+    xsets = [workloads.moe_tokens(dev), workloads.moe_tokens(dev, seed=502)]   # rotated, as in the moe step
     xq = torch.empty((T, K), dtype=torch.uint8, device=dev)
     xs = torch.empty((T, K // 128), dtype=torch.float32, device=dev)
     idx = tok.to(torch.int32).to(dev)
@@ -323,6 +328,7 @@ def moe_gather_workload(fb, dev):
     y = torch.empty((total_m, N), dtype=torch.bfloat16, device=dev)
 
     def launches(i):
+        x = xsets[i % 2]
         return [("quantize_x_1x128", lambda: fb.fp8_block_quantize(x, "1x128", "ceil", xq, xs)),
                 ("grouped_gemm_gather",
                  lambda: fb.fp8_grouped_gemm_gather(xq, xs, "1x128", idx, bq, sb, "1x32", offt, y))]

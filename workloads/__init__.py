@@ -77,13 +77,14 @@ def dense_projection(device="cpu", m=4096, n=2048, k=HIDDEN, seeds=(200, 201)):
     return {"w": w, "x": x}
 
 
-def qat_forward(device="cpu", m=8192, n=HIDDEN, k=HIDDEN, r=16):
+def qat_forward(device="cpu", m=8192, n=HIDDEN, k=HIDDEN, r=16, seed=300):
     """QAT fake-quant forward: base W [n, k] N(0, 0.02), LoRA A [r, k] and
-    B [n, r] N(0, 0.01), activations X [m, k] as the dense projection."""
-    w = normal_bf16((n, k), 0.02, 300, device)
-    a = normal_bf16((r, k), 0.01, 301, device)
-    b = normal_bf16((n, r), 0.01, 302, device)
-    x = normal_bf16((m, k), 1.0, 303, device, 0.01, 50.0, outlier_channels=True)
+    B [n, r] N(0, 0.01), activations X [m, k] as the dense projection
+    (seeds seed .. seed+3)."""
+    w = normal_bf16((n, k), 0.02, seed, device)
+    a = normal_bf16((r, k), 0.01, seed + 1, device)
+    b = normal_bf16((n, r), 0.01, seed + 2, device)
+    x = normal_bf16((m, k), 1.0, seed + 3, device, 0.01, 50.0, outlier_channels=True)
     return {"w": w, "lora_a": a, "lora_b": b, "x": x}
 
 
@@ -139,6 +140,6 @@ def zipf_routing(tokens=16384, n_experts=N_EXPERTS, top_k=TOP_K, s=1.1, seed=501
     return tok[order], offsets.to(torch.int32)
 
 
-def moe_tokens(device="cpu", tokens=16384):
-    """MoE activations X [tokens, 7168] N(0,1) with 1% channels x50 (seed 500)."""
-    return normal_bf16((tokens, HIDDEN), 1.0, 500, device, 0.01, 50.0, outlier_channels=True)
+def moe_tokens(device="cpu", tokens=16384, seed=500):
+    """MoE activations X [tokens, 7168] N(0,1) with 1% channels x50."""
+    return normal_bf16((tokens, HIDDEN), 1.0, seed, device, 0.01, 50.0, outlier_channels=True)
