@@ -14,8 +14,11 @@
 //     q = RN(q0 + r*y).  Blocks with amax < 2^-60 are pre-scaled by 2^64 so
 //     that the remainder never underflows; an exhaustive sweep over every
 //     bf16 pair (x, amax) found no input whose e4m3 code differs from the
-//     one the IEEE quotient gives.  The sign of x is re-inserted because
-//     the correction turns -0 into +0.
+//     one the IEEE quotient gives.  The remainder is formed negated,
+//     -r = RN(q0*s - x), and applied as q = RN((-r)*(-y) + q0): for x != 0
+//     that is the same exact value, so the same rounding, and for x = -0 it
+//     keeps the sign (-r = +0, and (+0)*(-y) + (-0) = -0), where the plain
+//     form gives +0; so no separate sign fix is needed.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -113,22 +116,21 @@ __device__ __forceinline__ F32Block f32_block(uint32_t amax_bits) {
   return b;
 }
 
-// RN32(x / s) with the sign of x (also for x = -0).
+// RN32(x / s) with the sign of x (also for x = -0: x*pre, q0 and q keep
+// it, and the negated remainder is +0).
 __device__ __forceinline__ float f32_quot(float x, const F32Block& b) {
   float xp = x * b.pre;
   float q0 = xp * b.y;
-  float r = __builtin_fmaf(-q0, b.sp, xp);
-  float q = __builtin_fmaf(r, b.y, q0);
-  return __uint_as_float((__float_as_uint(q) & 0x7FFFFFFFu) | (__float_as_uint(x) & 0x80000000u));
+  float rn = __builtin_fmaf(q0, b.sp, -xp);   // -r, exact
+  return __builtin_fmaf(rn, -b.y, q0);
 }
 
 // f32_quot for a block whose prescale is 1 (amax >= 2^-60): the same
 // operations without the multiplications by 1.
 __device__ __forceinline__ float f32_quot_unit(float x, const F32Block& b) {
   float q0 = x * b.y;
-  float r = __builtin_fmaf(-q0, b.sp, x);
-  float q = __builtin_fmaf(r, b.y, q0);
-  return __uint_as_float((__float_as_uint(q) & 0x7FFFFFFFu) | (__float_as_uint(x) & 0x80000000u));
+  float rn = __builtin_fmaf(q0, b.sp, -x);    // -r, exact
+  return __builtin_fmaf(rn, -b.y, q0);
 }
 
 // ---------------------------------------------------------------- E8M0 scale

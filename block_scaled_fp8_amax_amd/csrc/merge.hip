@@ -61,51 +61,71 @@ __global__ __launch_bounds__(256) void merge_128_kernel(const uint16_t* __restri
   const int64_t blk = row0 * k + (int64_t)blockIdx.x * 128;
   const uint32_t lofs = (uint32_t)((wv * 32 + lr) * k + lc * CPL);
   const uint32_t jstep = (uint32_t)(RPI * k);
-  const uint8_t* wb = reinterpret_cast<const uint8_t*>(w + blk);   // byte offsets 2 * o
+  const uint8_t* wb = reinterpret_cast<const uint8_t*>(w + blk);
 
   // Loads in the order B block, A columns, W rows, with compiler barriers
   // between the groups: B's LDS stores then wait only for B, and the merge
   // waits for each W row as it arrives.
+  // A rank-r block of B (r == RMAX) is 128 * RMAX contiguous bf16: thread
+  // t takes dwords [t * BPT / 2, (t + 1) * BPT / 2) of it.  Otherwise
+  // thread t takes elements t, t + 256, ... of the RMAX-padded block.
   constexpr int BPT = 128 * RMAX / 256;   // B elements per thread
   uint32_t braw[BPT];
   // (every load is issued, at a clamped rank below r, so that none waits
   // behind a branch; ranks >= r are then zeroed)
+  if constexpr (FULL) {
+    const uint32_t* bblk = reinterpret_cast<const uint32_t*>(lb + row0 * RMAX);   // wave-uniform
 #pragma unroll
-  for (int n = 0; n < BPT; ++n) {
-    const int i = t + 256 * n;
-    const int rr = i / RMAX, cc = i % RMAX;
-    if constexpr (FULL)
-      braw[n] = (uint32_t)lb[(row0 + rr) * RMAX + cc];
-    else
+    for (int n = 0; n < BPT / 2; ++n) braw[n] = bblk[t * (BPT / 2) + n];
+  } else {
+#pragma unroll
+    for (int n = 0; n < BPT; ++n) {
+      const int i = t + 256 * n;
+      const int rr = i / RMAX, cc = i % RMAX;
       braw[n] = (uint32_t)lb[(row0 + rr) * r + (cc < r ? cc : r - 1)];
+    }
   }
   asm volatile("" ::: "memory");
+  // A's rows as 32-bit byte offsets from the block's wave-uniform column
+  // base (rank * k * 2 < 2^31 for k <= 2^24, r <= 64), so that each load
+  // takes a scalar base and one vector add
   uint32_t araw[RMAX][DW];
+  const uint8_t* la_blk = reinterpret_cast<const uint8_t*>(la + (int64_t)blockIdx.x * 128);
+  const uint32_t lcol_b = (uint32_t)(lc * CPL * 2);
 #pragma unroll
   for (int i = 0; i < RMAX; ++i) {
     const int ic = FULL ? i : (i < r ? i : r - 1);
+    const uint32_t ao = (uint32_t)ic * (uint32_t)k * 2u + lcol_b;
     // dword loads: lora_a is only required to be 4-byte aligned
 #pragma unroll
-    for (int d = 0; d < DW; ++d) araw[i][d] = *reinterpret_cast<const uint32_t*>(la + (int64_t)ic * k + col + 2 * d);
+    for (int d = 0; d < DW; ++d) araw[i][d] = *reinterpret_cast<const uint32_t*>(la_blk + ao + 4 * d);
   }
   asm volatile("" ::: "memory");
   uint32_t wp[32];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
-    const uint32_t o = lofs + j * jstep;
+    const uint32_t ob = 2 * lofs + j * (2 * jstep);   // byte offset of the lane's bf16
     if constexpr (DW == 2) {
-      const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(wb + 2 * o));
+      const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(wb + ob));
       wp[2 * j] = v.x;
       wp[2 * j + 1] = v.y;
     } else {
-      wp[j] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(wb + 2 * o));
+      wp[j] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(wb + ob));
     }
   }
   asm volatile("" ::: "memory");
+  if constexpr (FULL) {
 #pragma unroll
-  for (int n = 0; n < BPT; ++n) {
-    const int cc = (t + 256 * n) % RMAX;
-    sB[t + 256 * n] = (FULL || cc < r) ? __uint_as_float(braw[n] << 16) : 0.f;
+    for (int n = 0; n < BPT / 2; ++n) {
+      sB[t * BPT + 2 * n] = bf_lo(braw[n]);
+      sB[t * BPT + 2 * n + 1] = bf_hi(braw[n]);
+    }
+  } else {
+#pragma unroll
+    for (int n = 0; n < BPT; ++n) {
+      const int cc = (t + 256 * n) % RMAX;
+      sB[t + 256 * n] = cc < r ? __uint_as_float(braw[n] << 16) : 0.f;
+    }
   }
   float a[RMAX][CPL];
 #pragma unroll
@@ -121,8 +141,10 @@ __global__ __launch_bounds__(256) void merge_128_kernel(const uint16_t* __restri
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 
-  // 4. merge in place: W' = RN_bf16(W + RN_bf16(sum_r B[n,r] A[r,k]))
-  uint32_t m = 0;
+  // 4. merge in place: W' = RN_bf16(W + RN_bf16(sum_r B[n,r] A[r,k])).
+  // The block amax runs on the packed bf16 magnitudes, one 16-bit max per
+  // half of a dword, and the two halves meet once at the end.
+  v2u16 m2 = {0, 0};
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int rr = wv * 32 + j * RPI + lr;
@@ -140,14 +162,17 @@ __global__ __launch_bounds__(256) void merge_128_kernel(const uint16_t* __restri
     }
 #pragma unroll
     for (int d = 0; d < DW; ++d) {
-      const uint32_t dl = pack_bf16x2(acc[2 * d], acc[2 * d + 1]);
+      // RN_bf16(acc) as an fp32 directly: the bf16 lands in the high half
+      // of the conversion's result, above a zero low half
+      const float d0 = __uint_as_float(pack_bf16x2(0.f, acc[2 * d]));
+      const float d1 = __uint_as_float(pack_bf16x2(0.f, acc[2 * d + 1]));
       const uint32_t w2 = wp[j * DW + d];
-      const uint32_t s2 = pack_bf16x2(bf_lo(w2) + bf_lo(dl), bf_hi(w2) + bf_hi(dl));
+      const uint32_t s2 = pack_bf16x2(bf_lo(w2) + d0, bf_hi(w2) + d1);
       wp[j * DW + d] = s2;
-      const uint32_t mm = absmax_bits<1>(&s2);
-      m = m > mm ? m : mm;
+      m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(v2u16, s2 & 0x7FFF7FFFu));
     }
   }
+  uint32_t m = m2[0] > m2[1] ? (uint32_t)m2[0] : (uint32_t)m2[1];
   m = wave_max(m);
   if (lane == 0) red[wv] = m;
   __syncthreads();
@@ -165,7 +190,7 @@ __global__ __launch_bounds__(256) void merge_128_kernel(const uint16_t* __restri
     constexpr bool TINY = decltype(tiny)::value;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-      const uint32_t o = lofs + j * jstep;
+      const uint32_t o = lofs + j * jstep;   // element (= code byte) offset; bf16 at 2 * o
       // the lane's codes in one dword: the first pair in the low half, the
       // second (4 columns per lane) in the high half of the same register
       uint32_t cw;
