@@ -47,6 +47,35 @@ def test_ranks(r):
     assert_bytes_equal(wdq, owdq, "dequant")
 
 
+def test_rank16_tiny_and_mixed_blocks():
+    """Rank 16 with blocks whose merged amax is below 2^-60 (the pre-scaled
+    quotient), blocks of exact zeros and signed zeros, next to ordinary ones."""
+    n, k, r = 384, 512, 16
+    wb, bb, ab = _bits((n, k), 0.02, 21), _bits((n, r), 0.01, 22, 4), _bits((r, k), 0.01, 23, 4)
+    wf = codec.bf16_to_f32(wb)
+    wf[0:128, 128:256] *= np.float32(2.0 ** -80)        # tiny W block (0, 1)
+    wf[128:256, 256:384] = 0.0                          # W zero, LoRA term alone: block (1, 2)
+    wf[256:384, 128:256] = 0.0                          # W and LoRA zero: block (2, 1)
+    wb = codec.f32_to_bf16(wf)
+    wb[256:384, 384:512] = 0x8000                       # W = -0, no LoRA term: block (2, 3)
+    bf = codec.bf16_to_f32(bb)
+    bf[0:128] *= np.float32(2.0 ** -40)                 # tiny LoRA update in block row 0
+    bf[256:384] = 0.0                                   # no update in block row 2
+    bb = codec.f32_to_bf16(bf)
+    af = codec.bf16_to_f32(ab)
+    af[:, 0:256] *= np.float32(2.0 ** -40)              # with A: 2^-80 below the rest
+    ab = codec.f32_to_bf16(af)
+    print(f"[merge] r=16 tiny/zero blocks {n}x{k}", flush=True)
+    for dq in (True, False):
+        q, s, wdq = _run(bf16_from_bits(wb), bf16_from_bits(bb), bf16_from_bits(ab), dequant=dq)
+        oq, os_, owdq = merge.fake_quant_merge(wb, bb, ab)
+        assert_bytes_equal(q, oq, "codes")
+        assert_bytes_equal(s, os_, "scales")
+        if dq:
+            assert_bytes_equal(wdq, owdq, "dequant")
+    assert (os_ < 2.0 ** -60).any() and (os_ == 0).any()
+
+
 def test_zero_lora_equals_quantize():
     wb = _bits((384, 256), 0.02, 4)
     w = bf16_from_bits(wb)
