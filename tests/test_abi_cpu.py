@@ -117,6 +117,8 @@ def test_merge_validation(lib):
     assert m(A16, A16, A16, 0, 128, 16, A16, A16, None, None) == OK
     assert m(A16, None, A16, 128, 128, 16, A16, A16, None, None) == INVALID
     assert m(A16 + 2, A16, A16, 128, 128, 16, A16, A16, None, None) == ALIGN
+    assert m(A16, A16 + 2, A16, 128, 128, 16, A16, A16, None, None) == ALIGN    # lora_b: 4 B (dword reads)
+    assert m(A16, A16, A16 + 2, 128, 128, 16, A16, A16, None, None) == ALIGN    # lora_a: 4 B
 
 
 def test_gemm_validation(lib):
