@@ -132,9 +132,10 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
 }
 
 // Grouped tile order.  Every workgroup builds, in LDS, the number of
-// m-tiles of each group (ceil(M_g / BM)) and their prefix sums; the tiles
-// of group g are numbered after those of groups 0..g-1, banded inside the
-// group like the dense order.  Consecutive runs of tiles ("windows", one
+// m-tiles of each group (ceil(M_g / BM)) and their prefix sums over the
+// groups in zig-zag order (below); a group's tiles are numbered after those
+// of the groups before it in that order, banded inside the group like the
+// dense order.  Consecutive runs of tiles ("windows", one
 // tile per CU of an XCD) share A rows and B columns; window w runs on XCD
 // w mod 8, so each XCD sees a mix of large (compute-bound) and small
 // (memory-bound) groups.  The grid is persistent: one workgroup per CU;
@@ -151,17 +152,26 @@ __device__ __forceinline__ void group_rows(const GemmParams& p, int g, int* lo, 
   *hi = clamp_int(p.offsets[g + 1], *lo, total);
 }
 
-// s_incl: LDS of `groups` ints, s_incl[g] = m-tiles of groups 0..g (the
-// m-tiles before group g are s_incl[g - 1], 0 for g = 0); returns the tile
-// count.
+// Groups are taken in zig-zag order of their index (0, G-1, 1, G-2, ...):
+// when the group sizes rise or fall with the index, as with experts
+// numbered by popularity, large groups (compute-bound tiles that reuse
+// their weights) then run beside small ones (tiles that stream their
+// weights once), instead of all large groups first and all small ones
+// last (Zipf-routed MoE GEMMs: gate||up 4.78 to 4.70 ms, down projection
+// 2.64 to 2.60 ms, bit-identical).  Position q holds group zigzag_group(q).
+__device__ __forceinline__ int zigzag_group(int q, int groups) { return (q & 1) ? groups - 1 - (q >> 1) : (q >> 1); }
+
+// s_incl: LDS of `groups` ints, s_incl[q] = m-tiles of the groups at
+// positions 0..q (the m-tiles before position q are s_incl[q - 1], 0 for
+// q = 0); returns the tile count.
 template <int BM>
 __device__ __forceinline__ int grouped_prefix(const GemmParams& p, int* s_incl, int nthreads) {
   const int groups = p.groups;
   const int t = threadIdx.x;
-  for (int g = t; g < groups; g += nthreads) {
+  for (int q = t; q < groups; q += nthreads) {
     int lo, hi;
-    group_rows(p, g, &lo, &hi);
-    s_incl[g] = (hi - lo + BM - 1) / BM;
+    group_rows(p, zigzag_group(q, groups), &lo, &hi);
+    s_incl[q] = (hi - lo + BM - 1) / BM;
   }
   __syncthreads();
   for (int d = 1; d < groups; d <<= 1) {  // inclusive scan
@@ -182,14 +192,15 @@ __device__ __forceinline__ void grouped_locate(const GemmParams& p, const int* s
                                                int* g_out, int64_t* row0, int* rows, int* tn_out) {
   const int tiles_n = p.tiles_n;
   const int slot = L / tiles_n;
-  int lo = 0, hi = p.groups - 1;  // g with s_incl[g - 1] <= slot < s_incl[g]
+  int lo = 0, hi = p.groups - 1;  // position q with s_incl[q - 1] <= slot < s_incl[q]
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
     if (s_incl[mid - 1] <= slot) lo = mid; else hi = mid - 1;
   }
-  const int g = lo;
-  const int before = g > 0 ? s_incl[g - 1] : 0;
-  const int tmg = s_incl[g] - before;
+  const int qpos = lo;
+  const int g = zigzag_group(qpos, p.groups);
+  const int before = qpos > 0 ? s_incl[qpos - 1] : 0;
+  const int tmg = s_incl[qpos] - before;
   const int r = L - before * tiles_n;
   const int band = p.band > 0 && p.band < tmg ? p.band : tmg;
   const int per_band = band * tiles_n;
