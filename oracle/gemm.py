@@ -12,7 +12,7 @@ weights and activations ([FP8-DSV3-ru] "Инференс с FP8"); routed MoE
 experts are the tensors served in MXFP8 ([prequant] "Formats" and the
 routed-expert rule below it).
 
-What the GEMM computes (reading, listed in the design doc): Y = A_hat . B_hat^T
+What the GEMM computes (a reading of the pages): Y = A_hat . B_hat^T
 with both operands stored K-contiguous ([M, K] and [N, K]), where
 A_hat = RN32(decode(qa) * sa) and B_hat = RN32(decode(qb) * sb) are the
 dequantized fp32 operands (exact for E8M0 scales).  The reference result is

@@ -8,7 +8,7 @@ bfloat16 ([Fireworks-QAT] Synopsis, Interpretation).  The forward GEMM is
 Y = X_hat . W_hat^T with W_hat = fakequant(W + B.A) and X_hat the
 fake-quantized activations.
 
-Reading (the pages name no gradient rule; listed in the design doc): the
+Reading (the pages name no gradient rule): the
 fake-quant is passed straight through in the backward pass (its Jacobian
 is taken as the identity), so with dY = dL/dY
 

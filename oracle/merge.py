@@ -10,8 +10,8 @@ weight is converted to block-wise FP8 ([Fireworks-QAT] "Synopsis",
 128x128 block with an fp32 scale inverse ([FP8-DSV3-ru] "Почему обычное
 округление не подходит").
 
-Reading of "merge W + B.A in bf16" (the pages print no formula; listed in
-the design doc): the bf16 product B.A is a rank-r sum accumulated in fp32 in the
+Reading of "merge W + B.A in bf16" (the pages print no formula): the bf16
+product B.A is a rank-r sum accumulated in fp32 in the
 order r = 0, 1, ..., R-1, each step one correctly rounded fp32
 multiply-add of an exact bf16 x bf16 product,
     acc_0 = 0,   acc_{r+1} = RN32(acc_r + B[n, r] * A[r, k]),

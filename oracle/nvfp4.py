@@ -3,8 +3,7 @@
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
 The page ([prequant] "Formats") names the format ``nvfp4`` as packed FP4
-values with FP8 block scales, served at FP4, and says no more.  Readings
-(each listed in the design doc):
+values with FP8 block scales, served at FP4, and says no more.  Readings:
   * FP4 element: E2M1 of the public OCP Microscaling specification -- sign,
     2 exponent bits with bias 1, 1 mantissa bit; magnitudes 0, 0.5, 1, 1.5,
     2, 3, 4, 6; no Inf or NaN.  Two codes per byte: element 2j of a row in

@@ -15,7 +15,7 @@ What the pages fix:
     weight plus a uint8 ``weight_scale_inv`` ([prequant] "Quick start",
     "Formats").
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
   * the scale comes from the block's largest magnitude (amax);
   * fp32 kinds store the dequantization multiplier s = RN32(amax / 448) and
     each element is encoded as e4m3(RN32(x / s)) -- an fp32 quotient, then

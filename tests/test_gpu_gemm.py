@@ -1,6 +1,6 @@
 """GPU parity of fp8_block_scaled_gemm and fp8_grouped_gemm against the oracle.
 
-Tolerance (spec metric, reading of the error bound in the design doc): with
+Tolerance (the stated error bound of the block-scaled GEMM): with
 fp32 output, max|Y - ref32| / max|ref32| <= 2e-3 where ref32 is the oracle's
 fp32-accumulated product of the same dequantized operands; the bf16 output
 must equal RN_bf16 of the kernel's own fp32 output bit for bit and lie within

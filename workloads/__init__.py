@@ -9,7 +9,7 @@ intermediate 2048, 256 routed experts, top-8 routing); the pages describe
 the model (671B parameters, about 37B active per token) and its MXFP8
 routed-expert checkpoints but ship no tensors, so every input is drawn here.
 
-Recipe (stated again in the design doc):
+Recipe:
   * values: torch.randn(float32) with a ``torch.Generator`` seeded per tensor
     on the target device, times sigma, times the outlier factor, then
     rounded to bf16 (RNE, torch ``.to(bfloat16)``);
